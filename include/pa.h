@@ -1,0 +1,212 @@
+/*
+ * pa.h -- C ABI of libpa: paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * Two layers, as the pages split the method ("vLLM explained", jackchen890311.github.io,
+ * section on the two implementation layers):
+ *   1. a memory manager: fixed-size blocks, per-sequence block tables, allocation on
+ *      demand, release, reference counts and copy-on-write (host, C++);
+ *   2. kernels that read K/V by jumping through the block table (HIP, gfx950).
+ *
+ * Conventions shared by every call
+ *   - Return value: PA_OK (0) or a negative PA_E_* code; the message for the last error
+ *     on the calling thread is returned by pa_last_error().  Calls returning int64_t
+ *     return a negative PA_E_* code on error.
+ *   - Ownership: every device buffer is allocated and freed by the caller.  The library
+ *     owns only the host-side pa_pool object (descriptor plus manager state).
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device calls only enqueue work; they never synchronize or read device memory
+ *     back.  Launch failures are reported as PA_E_HIP.
+ *   - Validation: host-side arguments are checked (null pointers, sizes, supported
+ *     shapes).  Device-resident indices (block tables, context lengths, slots, copy
+ *     pairs) are trusted to be in range, but the kernels never access memory outside
+ *     the pool for out-of-range values: see each call.
+ *   - Threading: a pa_pool is not thread-safe; calls on one pool must be serialized.
+ *
+ * Cache layout (one pool, caller memory at dev_base):
+ *     [num_layers][2 (K, V)][num_blocks][num_kv_heads][block_size][head_dim]
+ *   elements of kv_dtype.  One block id addresses the same block in every layer, which
+ *   is why a block's byte size carries the layer count ("vLLM explained", block-size
+ *   section, block-byte formula).  Inside a block the layout is head-major, so the
+ *   block_size x head_dim tile of one KV head is one contiguous run.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PA_OK = 0,
+  PA_E_INVAL = -1,       /* bad argument (null pointer, negative size, unknown id, ...) */
+  PA_E_NOMEM = -2,       /* the free list cannot cover the request; nothing changed     */
+  PA_E_HIP = -3,         /* a HIP runtime call or kernel launch failed                  */
+  PA_E_UNSUPPORTED = -4, /* valid but not implemented shape (see each call)              */
+  PA_E_RANGE = -5        /* an output buffer or capacity is too small                    */
+};
+
+enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
+
+typedef struct {
+  int32_t num_layers;   /* >= 1                                   */
+  int32_t num_blocks;   /* N physical blocks, >= 1                */
+  int32_t block_size;   /* tokens per block, >= 1                 */
+  int32_t num_kv_heads; /* >= 1                                   */
+  int32_t head_dim;     /* >= 1 (the attention kernels need 128)  */
+  int32_t kv_dtype;     /* PA_F32, PA_F16 or PA_BF16              */
+} pa_pool_desc;
+
+typedef struct pa_pool pa_pool; /* opaque, host-side, owned by the library */
+
+/* ---------------------------------------------------------------- sizes
+ * pa_block_bytes: bytes of one physical block across all layers, K and V:
+ *   2 * block_size * num_layers * num_kv_heads * head_dim * element bytes
+ *   ("vLLM explained", block-size section, block-byte formula; e.g. 8,388,608 B for a
+ *   Llama-2-7B-shaped fp16 cache with 16-token blocks).
+ * pa_pool_bytes: num_blocks * pa_block_bytes.  Both return PA_E_INVAL for a bad desc. */
+int64_t pa_block_bytes(const pa_pool_desc* desc);
+int64_t pa_pool_bytes(const pa_pool_desc* desc);
+
+/* ---------------------------------------------------------------- pool
+ * pa_alloc_pool: binds `dev_bytes` bytes of caller device memory at `dev_base`
+ *   (256-byte aligned, dev_bytes >= pa_pool_bytes) and builds the block manager over
+ *   the desc's num_blocks blocks.  `initial_free_order` (host, num_blocks entries, a
+ *   permutation of 0..N-1, or NULL for 0,1,2,...) is the order in which free blocks
+ *   are handed out.  With dev_base == NULL and dev_bytes == 0 the pool is host-only:
+ *   the manager works and every device call returns PA_E_INVAL.  Nothing is written
+ *   to device memory.  The caller keeps the memory alive until pa_free_pool.
+ * pa_free_pool: releases the host object only (NULL is accepted).
+ * pa_pool_layer_ptrs: device addresses of layer `layer`'s K and V
+ *   [num_blocks][num_kv_heads][block_size][head_dim] arrays. */
+int pa_alloc_pool(const pa_pool_desc* desc, void* dev_base, int64_t dev_bytes,
+                  const int32_t* initial_free_order, pa_pool** out);
+int pa_free_pool(pa_pool* pool);
+int pa_pool_layer_ptrs(const pa_pool* pool, int32_t layer, void** k_base, void** v_base);
+
+/* ---------------------------------------------------------------- block manager (host)
+ * The KV cache is cut into fixed-size blocks that need not be contiguous; a block
+ * table maps each sequence's logical blocks to physical ones; blocks are taken on
+ * demand and returned when the sequence ends ("vLLM explained", PagedAttention
+ * section, items 1-4; "LLM inference optimization: KV cache & PagedAttention",
+ * carlstack.gravito.dev, section 三.1 and Fig. 1).  Sequences forked from one parent
+ * share physical blocks by reference count, and a shared block is copied only when
+ * a branch writes a different token into it (carlstack page, section 三.2).
+ *
+ * Rules where the pages are silent (all operations are deterministic):
+ *   - Free list: a LIFO stack; freed blocks are pushed in logical order.
+ *   - Append of n tokens at length L: if L % block_size != 0 and the last block's
+ *     reference count is > 1, that block is first copied (copy-on-write): a fresh
+ *     block p' is taken, the pair (p, p') is reported, p loses one reference and p'
+ *     replaces p in the table.  Full blocks are never copied.  Then each position
+ *     with pos % block_size == 0 takes a fresh block.  Token pos gets the slot
+ *     table[pos / block_size] * block_size + pos % block_size.
+ *   - All-or-nothing: PA_E_NOMEM (free list too short) or PA_E_RANGE (cow_cap too
+ *     small) leave the manager unchanged.
+ *   - Sequence ids are 0, 1, 2, ... in creation order and are never reused.
+ *
+ * pa_seq_new:    creates an empty sequence.
+ * pa_seq_append: appends n_tokens (>= 0) tokens; writes their slots to slots_out
+ *                (host, n_tokens entries) and the copy-on-write pairs (src, dst) to
+ *                cow_pairs_out (host, 2 * cow_cap entries; an append makes at most
+ *                one pair) with their count in *n_cow_out.
+ * pa_seq_fork:   new sequence with a copy of parent's table and length; every block
+ *                gains one reference.
+ * pa_seq_free:   drops one reference from each block in logical order; blocks that
+ *                reach zero go back on the free stack.  The id becomes invalid.
+ * pa_seq_length: the sequence's token count.
+ * pa_export_block_tables: for the n sequences in seqs (host), writes
+ *                tables_out[n][max_blocks] (physical ids, padded with -1) and
+ *                ctx_out[n] (lengths).  PA_E_RANGE if a table is longer than max_blocks.
+ * pa_block_refcount, pa_num_free_blocks: queries.
+ * pa_export_free_stack: free blocks in the order they will be handed out (next first);
+ *                PA_E_RANGE if cap is too small (*n_out is still set). */
+int pa_seq_new(pa_pool* pool, int32_t* seq_out);
+int pa_seq_append(pa_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                  int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out);
+int pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* child_out);
+int pa_seq_free(pa_pool* pool, int32_t seq);
+int pa_seq_length(const pa_pool* pool, int32_t seq, int32_t* len_out);
+int pa_export_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n,
+                           int32_t max_blocks, int32_t* tables_out, int32_t* ctx_out);
+int pa_block_refcount(const pa_pool* pool, int32_t block, int32_t* rc_out);
+int pa_num_free_blocks(const pa_pool* pool, int32_t* n_out);
+int pa_export_free_stack(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
+
+/* ---------------------------------------------------------------- device ops
+ * pa_reshape_and_cache: writes new tokens' K and V rows into their slots of layer
+ *   `layer` (a bit copy).  k, v: device [n_tokens][num_kv_heads][head_dim] in the
+ *   pool's dtype, contiguous.  slots: device int64 [n_tokens]; slot s goes to block
+ *   s / block_size, offset s % block_size; -1 means "skip this token".  Slots must be
+ *   distinct (two tokens writing one slot race).  Slots outside [0, num_blocks *
+ *   block_size) are skipped like -1, never written.  Blocks are filled on demand,
+ *   token by token ("vLLM explained", PagedAttention section, item 4; carlstack page,
+ *   section 三.1 figure: logical block 2 is placed in a block allocated on demand).
+ *   head_dim * element bytes must be a multiple of 16 (else PA_E_UNSUPPORTED). */
+int pa_reshape_and_cache(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                         const int64_t* slots, int32_t n_tokens, void* stream);
+
+/* pa_copy_blocks: copy-on-write data movement: for each pair (src, dst) in pairs
+ *   (device int32 [n_pairs][2]), block dst <- block src in every layer, K and V, all
+ *   slots (carlstack page, section 三.2 and Fig. 1: copy only when a branch writes a
+ *   different token).  The pairs run concurrently, so no dst may appear twice or also
+ *   appear as a src (pairs from one step of the manager satisfy this).  Pairs with an
+ *   id outside [0, num_blocks) are skipped. */
+int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* stream);
+
+/* Paged-attention decode of one layer: for each sequence s and query head h,
+ *     out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s
+ *   over the sequence's context_lens[s] cached tokens (the newest one included),
+ *   with K_s, V_s read from KV head h / (num_q_heads / num_kv_heads) by jumping
+ *   through the sequence's block table (carlstack page, section 二, attention formula;
+ *   "vLLM explained", two implementation layers: same result as ordinary attention).
+ *
+ * The work is split over partitions of `partition_tokens` consecutive tokens (0 =
+ * default 512; else a positive multiple of 64): one pass computes each partition's
+ * softmax statistics and normalized output (pa_decode_partitions), a second pass
+ * merges the partitions of each sequence with log-sum-exp weights (pa_decode_reduce).
+ * Sequences that fit one partition are finished by the first pass.  pa_decode runs
+ * both.  The result does not depend on which physical blocks hold the data: the
+ * summation order follows logical token order only.
+ *
+ *   q            device [num_seqs][num_q_heads][head_dim], pool dtype, contiguous
+ *   block_tables device int32 [num_seqs][max_blocks]; entries past a sequence's last
+ *                block are never read
+ *   context_lens device int32 [num_seqs], 0 <= context_lens[s] <= max_context
+ *   max_context  host bound on context_lens (sizes the grid and the workspace)
+ *   scale        softmax scale, usually 1/sqrt(head_dim)
+ *   out          device fp32 [num_seqs][num_q_heads][head_dim]; an empty sequence
+ *                gets zeros
+ *   workspace    device scratch of at least pa_decode_workspace_bytes(...) bytes
+ *                (partition partials); its contents need no initialization
+ * A sequence whose length exceeds max_context or max_blocks * block_size, or whose
+ * table holds an id outside [0, num_blocks), gets NaN outputs; nothing outside the
+ * pool is read.  Supported: head_dim 128; num_q_heads / num_kv_heads in {1, 2, 4, 8,
+ * 16}; any block_size that is a multiple of 16; all three dtypes (fp32 accumulation). */
+int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_context, int32_t partition_tokens);
+int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
+              int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+              const int32_t* context_lens, int32_t max_context, float scale,
+              int32_t partition_tokens, float* out, void* workspace, int64_t workspace_bytes,
+              void* stream);
+int pa_decode_partitions(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
+                         int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                         const int32_t* context_lens, int32_t max_context, float scale,
+                         int32_t partition_tokens, float* out, void* workspace,
+                         int64_t workspace_bytes, void* stream);
+int pa_decode_reduce(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
+                     int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                     const int32_t* context_lens, int32_t max_context, float scale,
+                     int32_t partition_tokens, float* out, void* workspace,
+                     int64_t workspace_bytes, void* stream);
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

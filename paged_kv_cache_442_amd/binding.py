@@ -1,0 +1,297 @@
+"""Thin ctypes binding over ``libpa.so`` (C ABI in ``include/pa.h``).
+
+Functions carry the C names and only marshal arguments: torch tensors become
+device pointers, the current torch stream becomes the ``hipStream_t``, host arrays
+become numpy buffers.  Every step of the computation runs in the library; if the
+library is missing the first call raises, there is no fallback.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+F32, F16, BF16 = 0, 1, 2
+
+PA_OK, PA_E_INVAL, PA_E_NOMEM, PA_E_HIP, PA_E_UNSUPPORTED, PA_E_RANGE = 0, -1, -2, -3, -4, -5
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+_lib = None
+
+
+class PAError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__("%s (code %d)" % (message, code))
+        self.code = code
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+_DECODE_ARGS = [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, ctypes.c_float, _I32, _P, _P,
+                _I64, _P]
+
+_SIGNATURES = {
+    "pa_block_bytes": (_I64, [ctypes.POINTER(PoolDesc)]),
+    "pa_pool_bytes": (_I64, [ctypes.POINTER(PoolDesc)]),
+    "pa_alloc_pool": (ctypes.c_int, [ctypes.POINTER(PoolDesc), _P, _I64, _PI32, ctypes.POINTER(_P)]),
+    "pa_free_pool": (ctypes.c_int, [_P]),
+    "pa_pool_layer_ptrs": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
+    "pa_seq_new": (ctypes.c_int, [_P, _PI32]),
+    "pa_seq_append": (ctypes.c_int, [_P, _I32, _I32, _PI64, _PI32, _I32, _PI32]),
+    "pa_seq_fork": (ctypes.c_int, [_P, _I32, _PI32]),
+    "pa_seq_free": (ctypes.c_int, [_P, _I32]),
+    "pa_seq_length": (ctypes.c_int, [_P, _I32, _PI32]),
+    "pa_export_block_tables": (ctypes.c_int, [_P, _PI32, _I32, _I32, _PI32, _PI32]),
+    "pa_block_refcount": (ctypes.c_int, [_P, _I32, _PI32]),
+    "pa_num_free_blocks": (ctypes.c_int, [_P, _PI32]),
+    "pa_export_free_stack": (ctypes.c_int, [_P, _PI32, _I32, _PI32]),
+    "pa_reshape_and_cache": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
+    "pa_copy_blocks": (ctypes.c_int, [_P, _P, _I32, _P]),
+    "pa_decode_workspace_bytes": (_I64, [_P, _I32, _I32, _I32, _I32]),
+    "pa_decode": (ctypes.c_int, _DECODE_ARGS),
+    "pa_decode_partitions": (ctypes.c_int, _DECODE_ARGS),
+    "pa_decode_reduce": (ctypes.c_int, _DECODE_ARGS),
+    "pa_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """Load ``libpa.so`` (once); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libpa.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(rc):
+    if rc < 0:
+        raise PAError(int(rc), lib().pa_last_error().decode())
+    return rc
+
+
+def _i32p(a):
+    return a.ctypes.data_as(_PI32)
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous GPU tensor (checked on the host)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must have dtype %s, not %s" % (name, dtype, t.dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def torch_dtype(kv_dtype):
+    import torch
+    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[kv_dtype]
+
+
+class Pool:
+    """A ``pa_pool*`` plus the caller-owned device tensor backing it (kept alive here)."""
+
+    def __init__(self, handle, desc, storage):
+        self.handle = handle
+        self.desc = desc
+        self.storage = storage
+
+    @property
+    def num_blocks(self):
+        return self.desc.num_blocks
+
+    @property
+    def block_size(self):
+        return self.desc.block_size
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.pa_free_pool(self.handle)
+            self.handle = None
+
+
+def make_desc(num_layers, num_blocks, block_size, num_kv_heads, head_dim, kv_dtype):
+    return PoolDesc(num_layers, num_blocks, block_size, num_kv_heads, head_dim, kv_dtype)
+
+
+def pa_block_bytes(desc):
+    return _check(lib().pa_block_bytes(ctypes.byref(desc)))
+
+
+def pa_pool_bytes(desc):
+    return _check(lib().pa_pool_bytes(ctypes.byref(desc)))
+
+
+def pa_alloc_pool(desc, storage=None, initial_free_order=None):
+    """Bind ``storage`` (a GPU tensor of at least ``pa_pool_bytes`` bytes) or, with
+    ``storage=None``, build a host-only pool (manager only)."""
+    order = None
+    if initial_free_order is not None:
+        order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+        if order.shape != (desc.num_blocks,):
+            raise ValueError("initial_free_order must have num_blocks entries")
+    if storage is None:
+        base, nbytes = None, 0
+    else:
+        base = _dev(storage, name="storage")
+        nbytes = storage.numel() * storage.element_size()
+    out = ctypes.c_void_p()
+    _check(lib().pa_alloc_pool(ctypes.byref(desc), base, nbytes,
+                               None if order is None else _i32p(order), ctypes.byref(out)))
+    return Pool(out, desc, storage)
+
+
+def pa_free_pool(pool):
+    if pool.handle:
+        _check(lib().pa_free_pool(pool.handle))
+        pool.handle = None
+
+
+def pa_pool_layer_ptrs(pool, layer):
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(lib().pa_pool_layer_ptrs(pool.handle, layer, ctypes.byref(k), ctypes.byref(v)))
+    return k.value, v.value
+
+
+def pa_seq_new(pool):
+    s = ctypes.c_int32()
+    _check(lib().pa_seq_new(pool.handle, ctypes.byref(s)))
+    return s.value
+
+
+def pa_seq_append(pool, seq, n_tokens):
+    """Returns ``(slots int64[n], cow_pairs list of (src, dst))``."""
+    slots = np.zeros(max(1, n_tokens), dtype=np.int64)
+    pairs = np.zeros(2, dtype=np.int32)
+    n_cow = ctypes.c_int32()
+    _check(lib().pa_seq_append(pool.handle, seq, n_tokens, slots.ctypes.data_as(_PI64),
+                               _i32p(pairs), 1, ctypes.byref(n_cow)))
+    return slots[:n_tokens], [(int(pairs[0]), int(pairs[1]))] if n_cow.value else []
+
+
+def pa_seq_fork(pool, parent):
+    c = ctypes.c_int32()
+    _check(lib().pa_seq_fork(pool.handle, parent, ctypes.byref(c)))
+    return c.value
+
+
+def pa_seq_free(pool, seq):
+    _check(lib().pa_seq_free(pool.handle, seq))
+
+
+def pa_seq_length(pool, seq):
+    n = ctypes.c_int32()
+    _check(lib().pa_seq_length(pool.handle, seq, ctypes.byref(n)))
+    return n.value
+
+
+def pa_export_block_tables(pool, seqs, max_blocks):
+    seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+    tables = np.zeros((max(1, len(seqs)), max(1, max_blocks)), dtype=np.int32)
+    ctx = np.zeros(max(1, len(seqs)), dtype=np.int32)
+    _check(lib().pa_export_block_tables(pool.handle, _i32p(seqs), len(seqs), max_blocks,
+                                        _i32p(tables), _i32p(ctx)))
+    return tables[:len(seqs), :max_blocks], ctx[:len(seqs)]
+
+
+def pa_block_refcount(pool, block):
+    rc = ctypes.c_int32()
+    _check(lib().pa_block_refcount(pool.handle, block, ctypes.byref(rc)))
+    return rc.value
+
+
+def pa_num_free_blocks(pool):
+    n = ctypes.c_int32()
+    _check(lib().pa_num_free_blocks(pool.handle, ctypes.byref(n)))
+    return n.value
+
+
+def pa_export_free_stack(pool):
+    cap = pool.num_blocks
+    out = np.zeros(max(1, cap), dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(lib().pa_export_free_stack(pool.handle, _i32p(out), cap, ctypes.byref(n)))
+    return out[:n.value]
+
+
+def pa_reshape_and_cache(pool, layer, k, v, slots, stream=None):
+    """k, v: GPU ``[n][H_kv][d]`` in the pool dtype; slots: GPU int64 ``[n]``."""
+    import torch
+    dt = torch_dtype(pool.desc.kv_dtype)
+    n = slots.numel()
+    if k.shape[0] != n or v.shape != k.shape:
+        raise ValueError("k, v and slots disagree on the token count")
+    _check(lib().pa_reshape_and_cache(pool.handle, layer, _dev(k, dt, "k"), _dev(v, dt, "v"),
+                                      _dev(slots, torch.int64, "slots"), n, _stream(stream)))
+
+
+def pa_copy_blocks(pool, pairs, stream=None):
+    """pairs: GPU int32 ``[n][2]`` of (src, dst)."""
+    import torch
+    n = pairs.shape[0] if pairs.numel() else 0
+    _check(lib().pa_copy_blocks(pool.handle, _dev(pairs, torch.int32, "pairs") if n else None, n,
+                                _stream(stream)))
+
+
+def pa_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_context, partition_tokens=0):
+    return _check(lib().pa_decode_workspace_bytes(pool.handle, num_seqs, num_q_heads, max_context,
+                                                  partition_tokens))
+
+
+def _decode(fn, pool, layer, q, block_tables, context_lens, max_context, scale, out, workspace,
+            partition_tokens, stream):
+    import torch
+    S, H_q = q.shape[0], q.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(fn(pool.handle, layer, _dev(q, torch_dtype(pool.desc.kv_dtype), "q"), S, H_q,
+              _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+              _dev(context_lens, torch.int32, "context_lens"), max_context, float(scale),
+              partition_tokens, _dev(out, torch.float32, "out"),
+              None if workspace is None else _dev(workspace, name="workspace"), ws_bytes,
+              _stream(stream)))
+
+
+def pa_decode(pool, layer, q, block_tables, context_lens, max_context, scale, out, workspace,
+              partition_tokens=0, stream=None):
+    """q: GPU ``[S][H_q][d]`` pool dtype; out: GPU fp32 ``[S][H_q][d]``."""
+    _decode(lib().pa_decode, pool, layer, q, block_tables, context_lens, max_context, scale, out,
+            workspace, partition_tokens, stream)
+
+
+def pa_decode_partitions(pool, layer, q, block_tables, context_lens, max_context, scale, out,
+                         workspace, partition_tokens=0, stream=None):
+    _decode(lib().pa_decode_partitions, pool, layer, q, block_tables, context_lens, max_context,
+            scale, out, workspace, partition_tokens, stream)
+
+
+def pa_decode_reduce(pool, layer, q, block_tables, context_lens, max_context, scale, out,
+                     workspace, partition_tokens=0, stream=None):
+    _decode(lib().pa_decode_reduce, pool, layer, q, block_tables, context_lens, max_context,
+            scale, out, workspace, partition_tokens, stream)

@@ -1,0 +1,100 @@
+// Host block manager (see block_manager.hpp for the rules and their sources).
+#include "block_manager.hpp"
+
+namespace pa {
+
+BlockManager::BlockManager(int32_t num_blocks, int32_t block_size,
+                           const std::vector<int32_t>& pop_order)
+    : num_blocks_(num_blocks), block_size_(block_size), refcount_(num_blocks, 0) {
+  free_stack_.reserve(num_blocks);
+  // The stack hands out its back() first, so push the pop order reversed.
+  for (int32_t i = num_blocks - 1; i >= 0; --i)
+    free_stack_.push_back(pop_order.empty() ? i : pop_order[i]);
+}
+
+bool BlockManager::live(int32_t seq) const {
+  return seq >= 0 && seq < static_cast<int32_t>(seqs_.size()) && seqs_[seq].live;
+}
+
+int32_t BlockManager::pop() {
+  int32_t b = free_stack_.back();
+  free_stack_.pop_back();
+  return b;
+}
+
+MgrStatus BlockManager::seq_new(int32_t* seq) {
+  if (seqs_.size() >= static_cast<size_t>(INT32_MAX)) return MgrStatus::range;
+  seqs_.emplace_back();
+  seqs_.back().live = true;
+  *seq = static_cast<int32_t>(seqs_.size() - 1);
+  return MgrStatus::ok;
+}
+
+MgrStatus BlockManager::seq_append(int32_t seq, int32_t n, int64_t* slots, int32_t* cow_pairs,
+                                   int32_t cow_cap, int32_t* n_cow) {
+  if (!live(seq) || n < 0) return MgrStatus::invalid;
+  Seq& s = seqs_[seq];
+  const int64_t L = s.length;
+  if (L + n > INT32_MAX) return MgrStatus::range;
+  const int64_t bs = block_size_;
+  // Work out every block this append takes before changing anything.
+  const bool cow = n > 0 && L % bs != 0 && refcount_[s.table.back()] > 1;
+  const int64_t fresh = (L + n + bs - 1) / bs - (L + bs - 1) / bs;
+  if (cow && cow_cap < 1) return MgrStatus::range;
+  if (fresh + (cow ? 1 : 0) > static_cast<int64_t>(free_stack_.size())) return MgrStatus::no_blocks;
+
+  *n_cow = 0;
+  if (cow) {
+    const int32_t shared = s.table.back();
+    const int32_t copy = pop();
+    refcount_[shared] -= 1;
+    refcount_[copy] = 1;
+    s.table.back() = copy;
+    cow_pairs[0] = shared;
+    cow_pairs[1] = copy;
+    *n_cow = 1;
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t pos = L + i;
+    if (pos % bs == 0) {
+      const int32_t b = pop();
+      refcount_[b] = 1;
+      s.table.push_back(b);
+    }
+    slots[i] = static_cast<int64_t>(s.table[pos / bs]) * bs + pos % bs;
+  }
+  s.length = static_cast<int32_t>(L + n);
+  return MgrStatus::ok;
+}
+
+MgrStatus BlockManager::seq_fork(int32_t parent, int32_t* child) {
+  if (!live(parent)) return MgrStatus::invalid;
+  int32_t id;
+  MgrStatus st = seq_new(&id);
+  if (st != MgrStatus::ok) return st;
+  Seq& c = seqs_[id];
+  const Seq& p = seqs_[parent];  // re-read: seq_new may have moved the vector
+  c.table = p.table;
+  c.length = p.length;
+  for (int32_t b : c.table) refcount_[b] += 1;
+  *child = id;
+  return MgrStatus::ok;
+}
+
+MgrStatus BlockManager::seq_free(int32_t seq) {
+  if (!live(seq)) return MgrStatus::invalid;
+  Seq& s = seqs_[seq];
+  for (int32_t b : s.table) {
+    if (--refcount_[b] == 0) free_stack_.push_back(b);
+  }
+  s.live = false;
+  s.length = 0;
+  std::vector<int32_t>().swap(s.table);
+  return MgrStatus::ok;
+}
+
+void BlockManager::free_stack_top_first(std::vector<int32_t>* out) const {
+  out->assign(free_stack_.rbegin(), free_stack_.rend());
+}
+
+}  // namespace pa

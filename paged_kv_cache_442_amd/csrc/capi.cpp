@@ -1,0 +1,428 @@
+// C ABI of libpa (declared in include/pa.h): argument checking, the pool object and
+// dispatch to the host block manager and the gfx950 kernels.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <limits>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "block_manager.hpp"
+#include "kernels.hpp"
+
+struct pa_pool {
+  pa_pool_desc desc;
+  char* dev_base;  // NULL for a host-only pool
+  int64_t dev_bytes;
+  int64_t elem_bytes;
+  int64_t array_bytes;  // one layer's K (or V): num_blocks * heads * block_size * head_dim * elem
+  std::unique_ptr<pa::BlockManager> mgr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() { return PA_OK; }
+
+int64_t elem_bytes_of(int32_t dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    default: return 0;
+  }
+}
+
+int check_desc(const pa_pool_desc* d) {
+  if (!d) return fail(PA_E_INVAL, "desc is NULL");
+  if (d->num_layers < 1 || d->num_blocks < 1 || d->block_size < 1 || d->num_kv_heads < 1 ||
+      d->head_dim < 1)
+    return fail(PA_E_INVAL, "desc fields must be >= 1 (layers %d blocks %d block_size %d heads %d dim %d)",
+                d->num_layers, d->num_blocks, d->block_size, d->num_kv_heads, d->head_dim);
+  if (elem_bytes_of(d->kv_dtype) == 0) return fail(PA_E_INVAL, "unknown kv_dtype %d", d->kv_dtype);
+  return PA_OK;
+}
+
+// Bytes of one block in one layer's K (or V) array, with overflow checking.
+bool array_block_bytes(const pa_pool_desc* d, int64_t* out) {
+  __int128 b = static_cast<__int128>(d->num_kv_heads) * d->block_size * d->head_dim *
+               elem_bytes_of(d->kv_dtype);
+  if (b > std::numeric_limits<int64_t>::max() / 4) return false;
+  *out = static_cast<int64_t>(b);
+  return true;
+}
+
+int mgr_status(pa::MgrStatus st, const char* what) {
+  switch (st) {
+    case pa::MgrStatus::ok: return ok();
+    case pa::MgrStatus::invalid: return fail(PA_E_INVAL, "%s: unknown or freed sequence, or bad count", what);
+    case pa::MgrStatus::no_blocks: return fail(PA_E_NOMEM, "%s: not enough free blocks", what);
+    case pa::MgrStatus::range: return fail(PA_E_RANGE, "%s: capacity exceeded", what);
+  }
+  return fail(PA_E_INVAL, "%s: unknown status", what);
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_device_pool(const pa_pool* p, int32_t layer) {
+  if (!p) return fail(PA_E_INVAL, "pool is NULL");
+  if (!p->dev_base) return fail(PA_E_INVAL, "pool is host-only (no device memory bound)");
+  if (layer < 0 || layer >= p->desc.num_layers)
+    return fail(PA_E_INVAL, "layer %d outside [0, %d)", layer, p->desc.num_layers);
+  return PA_OK;
+}
+
+struct DecodeCall {
+  pa::DecodeArgs args;
+  int group;
+};
+
+int prepare_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
+                   int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                   const int32_t* context_lens, int32_t max_context, float scale,
+                   int32_t partition_tokens, float* out, void* workspace, int64_t workspace_bytes,
+                   DecodeCall* call) {
+  int st = check_device_pool(pool, layer);
+  if (st) return st;
+  const pa_pool_desc& d = pool->desc;
+  if (num_seqs < 0 || num_q_heads < 1 || max_blocks < 0 || max_context < 0)
+    return fail(PA_E_INVAL, "negative size (num_seqs %d num_q_heads %d max_blocks %d max_context %d)",
+                num_seqs, num_q_heads, max_blocks, max_context);
+  if (num_q_heads % d.num_kv_heads != 0)
+    return fail(PA_E_INVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                d.num_kv_heads);
+  const int group = num_q_heads / d.num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PA_E_UNSUPPORTED, "query group size %d (supported: 1, 2, 4, 8)", group);
+  if (d.head_dim != pa::kHeadDim)
+    return fail(PA_E_UNSUPPORTED, "head_dim %d (supported: %d)", d.head_dim, pa::kHeadDim);
+  if (d.block_size % pa::kTileTokens != 0)
+    return fail(PA_E_UNSUPPORTED, "block_size %d (must be a multiple of %d)", d.block_size,
+                pa::kTileTokens);
+  if (partition_tokens == 0) partition_tokens = pa::kDefaultPartition;
+  if (partition_tokens < 0 || partition_tokens % (pa::kTileTokens * pa::kDecodeWaves) != 0)
+    return fail(PA_E_INVAL, "partition_tokens %d must be a positive multiple of %d", partition_tokens,
+                pa::kTileTokens * pa::kDecodeWaves);
+  if (!std::isfinite(scale)) return fail(PA_E_INVAL, "scale is not finite");
+  if (num_seqs == 0) {
+    call->args = pa::DecodeArgs{};
+    call->args.num_seqs = 0;
+    call->group = group;
+    return PA_OK;
+  }
+  if (!q || !block_tables || !context_lens || !out)
+    return fail(PA_E_INVAL, "q, block_tables, context_lens and out must be non-NULL");
+  if (num_seqs > 0x7fffffff / num_q_heads) return fail(PA_E_RANGE, "num_seqs * num_q_heads overflows");
+  const int64_t pmax = std::max<int64_t>(1, (static_cast<int64_t>(max_context) + partition_tokens - 1) /
+                                                partition_tokens);
+  if (pmax > 65535) return fail(PA_E_RANGE, "max_context %d needs %lld partitions (limit 65535)",
+                                max_context, static_cast<long long>(pmax));
+  if (d.num_kv_heads > 65535) return fail(PA_E_UNSUPPORTED, "more than 65535 KV heads");
+  const int64_t need = pa_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_context,
+                                                 partition_tokens);
+  if (need < 0) return static_cast<int>(need);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_E_RANGE, "workspace of %lld bytes is smaller than the %lld needed",
+                static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+  for (const void* ptr : {q, static_cast<const void*>(out), static_cast<const void*>(workspace)})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+      return fail(PA_E_INVAL, "q, out and workspace must be 16-byte aligned");
+
+  pa::DecodeArgs& a = call->args;
+  a.q = q;
+  a.k_cache = pool->dev_base + static_cast<int64_t>(2 * layer) * pool->array_bytes;
+  a.v_cache = pool->dev_base + static_cast<int64_t>(2 * layer + 1) * pool->array_bytes;
+  a.tables = block_tables;
+  a.ctx = context_lens;
+  a.out = out;
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = a.part_o ? a.part_o + rows * pmax * pa::kHeadDim : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = d.num_kv_heads;
+  a.max_blocks = max_blocks;
+  a.num_blocks = d.num_blocks;
+  a.block_size = d.block_size;
+  a.max_context = max_context;
+  a.partition_tokens = partition_tokens;
+  a.pmax = static_cast<int32_t>(pmax);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  call->group = group;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int64_t pa_block_bytes(const pa_pool_desc* desc) {
+  int st = check_desc(desc);
+  if (st) return st;
+  int64_t per_array;
+  if (!array_block_bytes(desc, &per_array)) return fail(PA_E_RANGE, "block bytes overflow");
+  __int128 b = static_cast<__int128>(per_array) * 2 * desc->num_layers;
+  if (b > std::numeric_limits<int64_t>::max()) return fail(PA_E_RANGE, "block bytes overflow");
+  return static_cast<int64_t>(b);
+}
+
+int64_t pa_pool_bytes(const pa_pool_desc* desc) {
+  int64_t b = pa_block_bytes(desc);
+  if (b < 0) return b;
+  __int128 p = static_cast<__int128>(b) * desc->num_blocks;
+  if (p > std::numeric_limits<int64_t>::max()) return fail(PA_E_RANGE, "pool bytes overflow");
+  return static_cast<int64_t>(p);
+}
+
+int pa_alloc_pool(const pa_pool_desc* desc, void* dev_base, int64_t dev_bytes,
+                  const int32_t* initial_free_order, pa_pool** out) {
+  if (!out) return fail(PA_E_INVAL, "out is NULL");
+  *out = nullptr;
+  int st = check_desc(desc);
+  if (st) return st;
+  const int64_t need = pa_pool_bytes(desc);
+  if (need < 0) return static_cast<int>(need);
+  if (dev_base) {
+    if (reinterpret_cast<uintptr_t>(dev_base) % 256 != 0)
+      return fail(PA_E_INVAL, "dev_base must be 256-byte aligned");
+    if (dev_bytes < need)
+      return fail(PA_E_RANGE, "dev_bytes %lld < pool bytes %lld", static_cast<long long>(dev_bytes),
+                  static_cast<long long>(need));
+  } else if (dev_bytes != 0) {
+    return fail(PA_E_INVAL, "dev_bytes must be 0 for a host-only pool");
+  }
+  std::vector<int32_t> order;
+  if (initial_free_order) {
+    order.assign(initial_free_order, initial_free_order + desc->num_blocks);
+    std::vector<char> seen(desc->num_blocks, 0);
+    for (int32_t b : order) {
+      if (b < 0 || b >= desc->num_blocks || seen[b])
+        return fail(PA_E_INVAL, "initial_free_order is not a permutation of 0..%d", desc->num_blocks - 1);
+      seen[b] = 1;
+    }
+  }
+  std::unique_ptr<pa_pool> p(new (std::nothrow) pa_pool);
+  if (!p) return fail(PA_E_NOMEM, "host allocation failed");
+  p->desc = *desc;
+  p->dev_base = static_cast<char*>(dev_base);
+  p->dev_bytes = dev_bytes;
+  p->elem_bytes = elem_bytes_of(desc->kv_dtype);
+  int64_t per_array_block;
+  array_block_bytes(desc, &per_array_block);
+  p->array_bytes = per_array_block * desc->num_blocks;
+  p->mgr.reset(new (std::nothrow) pa::BlockManager(desc->num_blocks, desc->block_size, order));
+  if (!p->mgr) return fail(PA_E_NOMEM, "host allocation failed");
+  *out = p.release();
+  return ok();
+}
+
+int pa_free_pool(pa_pool* pool) {
+  delete pool;
+  return ok();
+}
+
+int pa_pool_layer_ptrs(const pa_pool* pool, int32_t layer, void** k_base, void** v_base) {
+  int st = check_device_pool(pool, layer);
+  if (st) return st;
+  if (!k_base || !v_base) return fail(PA_E_INVAL, "k_base and v_base must be non-NULL");
+  *k_base = pool->dev_base + static_cast<int64_t>(2 * layer) * pool->array_bytes;
+  *v_base = pool->dev_base + static_cast<int64_t>(2 * layer + 1) * pool->array_bytes;
+  return ok();
+}
+
+int pa_seq_new(pa_pool* pool, int32_t* seq_out) {
+  if (!pool || !seq_out) return fail(PA_E_INVAL, "pool and seq_out must be non-NULL");
+  return mgr_status(pool->mgr->seq_new(seq_out), "pa_seq_new");
+}
+
+int pa_seq_append(pa_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                  int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out) {
+  if (!pool || !n_cow_out) return fail(PA_E_INVAL, "pool and n_cow_out must be non-NULL");
+  if (n_tokens > 0 && !slots_out) return fail(PA_E_INVAL, "slots_out is NULL");
+  if (cow_cap < 0 || (cow_cap > 0 && !cow_pairs_out)) return fail(PA_E_INVAL, "bad cow_pairs_out / cow_cap");
+  int32_t dummy_pair[2];
+  int32_t* pairs = cow_cap > 0 ? cow_pairs_out : dummy_pair;
+  int32_t n_cow = 0;
+  int st = mgr_status(pool->mgr->seq_append(seq, n_tokens, slots_out, pairs, cow_cap, &n_cow),
+                      "pa_seq_append");
+  if (st == PA_OK) *n_cow_out = n_cow;
+  return st;
+}
+
+int pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* child_out) {
+  if (!pool || !child_out) return fail(PA_E_INVAL, "pool and child_out must be non-NULL");
+  return mgr_status(pool->mgr->seq_fork(parent, child_out), "pa_seq_fork");
+}
+
+int pa_seq_free(pa_pool* pool, int32_t seq) {
+  if (!pool) return fail(PA_E_INVAL, "pool is NULL");
+  return mgr_status(pool->mgr->seq_free(seq), "pa_seq_free");
+}
+
+int pa_seq_length(const pa_pool* pool, int32_t seq, int32_t* len_out) {
+  if (!pool || !len_out) return fail(PA_E_INVAL, "pool and len_out must be non-NULL");
+  if (!pool->mgr->live(seq)) return fail(PA_E_INVAL, "unknown or freed sequence %d", seq);
+  *len_out = pool->mgr->length(seq);
+  return ok();
+}
+
+int pa_export_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n, int32_t max_blocks,
+                           int32_t* tables_out, int32_t* ctx_out) {
+  if (!pool || n < 0 || max_blocks < 0) return fail(PA_E_INVAL, "bad pool, n or max_blocks");
+  if (n > 0 && (!seqs || !ctx_out || (max_blocks > 0 && !tables_out)))
+    return fail(PA_E_INVAL, "seqs, tables_out and ctx_out must be non-NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    if (!pool->mgr->live(seqs[i])) return fail(PA_E_INVAL, "unknown or freed sequence %d", seqs[i]);
+    if (static_cast<int64_t>(pool->mgr->table(seqs[i]).size()) > max_blocks)
+      return fail(PA_E_RANGE, "sequence %d holds %zu blocks > max_blocks %d", seqs[i],
+                  pool->mgr->table(seqs[i]).size(), max_blocks);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const std::vector<int32_t>& t = pool->mgr->table(seqs[i]);
+    int32_t* row = tables_out + static_cast<int64_t>(i) * max_blocks;
+    for (int32_t j = 0; j < max_blocks; ++j) row[j] = j < static_cast<int32_t>(t.size()) ? t[j] : -1;
+    ctx_out[i] = pool->mgr->length(seqs[i]);
+  }
+  return ok();
+}
+
+int pa_block_refcount(const pa_pool* pool, int32_t block, int32_t* rc_out) {
+  if (!pool || !rc_out) return fail(PA_E_INVAL, "pool and rc_out must be non-NULL");
+  if (block < 0 || block >= pool->desc.num_blocks) return fail(PA_E_INVAL, "block %d out of range", block);
+  *rc_out = pool->mgr->refcount(block);
+  return ok();
+}
+
+int pa_num_free_blocks(const pa_pool* pool, int32_t* n_out) {
+  if (!pool || !n_out) return fail(PA_E_INVAL, "pool and n_out must be non-NULL");
+  *n_out = pool->mgr->num_free();
+  return ok();
+}
+
+int pa_export_free_stack(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out) {
+  if (!pool || !n_out || cap < 0 || (cap > 0 && !out)) return fail(PA_E_INVAL, "bad arguments");
+  std::vector<int32_t> v;
+  pool->mgr->free_stack_top_first(&v);
+  *n_out = static_cast<int32_t>(v.size());
+  if (static_cast<int64_t>(v.size()) > cap) return fail(PA_E_RANGE, "cap %d < %zu free blocks", cap, v.size());
+  for (size_t i = 0; i < v.size(); ++i) out[i] = v[i];
+  return ok();
+}
+
+int pa_reshape_and_cache(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                         const int64_t* slots, int32_t n_tokens, void* stream) {
+  int st = check_device_pool(pool, layer);
+  if (st) return st;
+  if (n_tokens < 0) return fail(PA_E_INVAL, "n_tokens < 0");
+  const int64_t row_bytes = static_cast<int64_t>(pool->desc.head_dim) * pool->elem_bytes;
+  if (row_bytes % 16 != 0)
+    return fail(PA_E_UNSUPPORTED, "head_dim * element bytes = %lld is not a multiple of 16",
+                static_cast<long long>(row_bytes));
+  if (n_tokens == 0) return ok();
+  if (!k || !v || !slots) return fail(PA_E_INVAL, "k, v and slots must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(k) % 16 || reinterpret_cast<uintptr_t>(v) % 16)
+    return fail(PA_E_INVAL, "k and v must be 16-byte aligned");
+  void *kc, *vc;
+  pa_pool_layer_ptrs(pool, layer, &kc, &vc);
+  const int64_t num_slots = static_cast<int64_t>(pool->desc.num_blocks) * pool->desc.block_size;
+  return hip_status(pa::launch_reshape_and_cache(k, v, slots, kc, vc, n_tokens, pool->desc.num_kv_heads,
+                                                 pool->desc.block_size, num_slots,
+                                                 static_cast<int32_t>(row_bytes),
+                                                 static_cast<hipStream_t>(stream)),
+                    "pa_reshape_and_cache");
+}
+
+int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* stream) {
+  int st = check_device_pool(pool, 0);
+  if (st) return st;
+  if (n_pairs < 0) return fail(PA_E_INVAL, "n_pairs < 0");
+  if (n_pairs == 0) return ok();
+  if (!pairs) return fail(PA_E_INVAL, "pairs is NULL");
+  if (2 * pool->desc.num_layers > 65535) return fail(PA_E_UNSUPPORTED, "too many layers");
+  const int64_t block_bytes = pool->array_bytes / pool->desc.num_blocks;
+  if (block_bytes % 16 != 0) return fail(PA_E_UNSUPPORTED, "per-layer block bytes not a multiple of 16");
+  return hip_status(pa::launch_copy_blocks(pairs, n_pairs, pool->dev_base, 2 * pool->desc.num_layers,
+                                           pool->desc.num_blocks, block_bytes,
+                                           static_cast<hipStream_t>(stream)),
+                    "pa_copy_blocks");
+}
+
+int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_context, int32_t partition_tokens) {
+  if (!pool) return fail(PA_E_INVAL, "pool is NULL");
+  if (num_seqs < 0 || num_q_heads < 0 || max_context < 0 || partition_tokens < 0)
+    return fail(PA_E_INVAL, "negative size");
+  if (partition_tokens == 0) partition_tokens = pa::kDefaultPartition;
+  const int64_t pmax = (static_cast<int64_t>(max_context) + partition_tokens - 1) / partition_tokens;
+  if (pmax <= 1) return 0;  // every sequence fits one partition: no partials
+  const __int128 b = static_cast<__int128>(num_seqs) * num_q_heads * pmax * (pa::kHeadDim + 1) * 4;
+  if (b > std::numeric_limits<int64_t>::max()) return fail(PA_E_RANGE, "workspace size overflows");
+  return static_cast<int64_t>(b);
+}
+
+int pa_decode_partitions(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
+                         int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                         const int32_t* context_lens, int32_t max_context, float scale,
+                         int32_t partition_tokens, float* out, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  DecodeCall c;
+  int st = prepare_decode(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+                          context_lens, max_context, scale, partition_tokens, out, workspace,
+                          workspace_bytes, &c);
+  if (st) return st;
+  if (c.args.num_seqs == 0) return ok();
+  return hip_status(pa::launch_decode_partitions(c.args, static_cast<int>(pool->desc.kv_dtype), c.group,
+                                                 static_cast<hipStream_t>(stream)),
+                    "pa_decode_partitions");
+}
+
+int pa_decode_reduce(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
+                     int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                     const int32_t* context_lens, int32_t max_context, float scale,
+                     int32_t partition_tokens, float* out, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+  DecodeCall c;
+  int st = prepare_decode(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+                          context_lens, max_context, scale, partition_tokens, out, workspace,
+                          workspace_bytes, &c);
+  if (st) return st;
+  if (c.args.num_seqs == 0 || c.args.pmax <= 1) return ok();
+  return hip_status(pa::launch_decode_reduce(c.args, static_cast<hipStream_t>(stream)),
+                    "pa_decode_reduce");
+}
+
+int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs, int32_t num_q_heads,
+              const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+              int32_t max_context, float scale, int32_t partition_tokens, float* out,
+              void* workspace, int64_t workspace_bytes, void* stream) {
+  int st = pa_decode_partitions(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+                                context_lens, max_context, scale, partition_tokens, out, workspace,
+                                workspace_bytes, stream);
+  if (st) return st;
+  return pa_decode_reduce(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+                          context_lens, max_context, scale, partition_tokens, out, workspace,
+                          workspace_bytes, stream);
+}
+
+}  // extern "C"

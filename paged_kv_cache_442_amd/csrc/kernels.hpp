@@ -1,0 +1,45 @@
+// Launchers for the gfx950 kernels (defined in kernels.hip).  Host-side only; every
+// pointer is device memory owned by the caller, every launch is asynchronous on
+// `stream`.  Argument checking happens in the C ABI layer (capi.cpp); these
+// functions assume valid, supported arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace pa {
+
+constexpr int kHeadDim = 128;        // head_dim the attention kernels are built for
+constexpr int kTileTokens = 16;      // tokens per K/V tile streamed by the decode kernel
+constexpr int kDecodeWaves = 4;      // waves per decode workgroup
+constexpr int kDefaultPartition = 512;
+
+struct DecodeArgs {
+  const void* q;            // [S][Hq][128]
+  const void* k_cache;      // one layer: [N][Hkv][bs][128]
+  const void* v_cache;
+  const int32_t* tables;    // [S][max_blocks]
+  const int32_t* ctx;       // [S]
+  float* out;               // [S][Hq][128]
+  float* part_o;            // [S][Hq][pmax][128]
+  float* part_lse;          // [S][Hq][pmax], base-2 log-sum-exp of scaled scores
+  int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks, num_blocks, block_size;
+  int32_t max_context, partition_tokens, pmax;
+  float scale_log2;         // scale * log2(e)
+};
+
+// dtype: 0 fp32, 1 fp16, 2 bf16; group = num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+hipError_t launch_decode_partitions(const DecodeArgs& a, int dtype, int group, hipStream_t s);
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t s);
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, const int64_t* slots,
+                                    void* k_cache, void* v_cache, int32_t n_tokens,
+                                    int32_t num_kv_heads, int32_t block_size, int64_t num_slots,
+                                    int32_t row_bytes, hipStream_t s);
+
+// base: pool base, holding `arrays` (= 2 * num_layers) arrays, each of num_blocks blocks of
+// block_bytes bytes (one layer's K or V part of a block).
+hipError_t launch_copy_blocks(const int32_t* pairs, int32_t n_pairs, void* base, int32_t arrays,
+                              int32_t num_blocks, int64_t block_bytes, hipStream_t s);
+
+}  // namespace pa
