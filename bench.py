@@ -1,0 +1,237 @@
+"""Paged-attention decode benchmark on one MI355X.
+
+A step is one decode step of one layer over the whole batch: the newest token of
+every sequence is written into its slot (``pa_reshape_and_cache``), then
+``pa_decode`` runs its two kernels (per-partition attention, log-sum-exp merge).
+Inputs (pool, tables, queries) are resident in HBM before timing starts.
+
+The JSON line reports:
+  value      algorithmic K+V+Q bytes per step / step time, in GB/s;
+  roofline   the partition kernel's algorithmic bytes / its mean duration
+             (HIP events on the launch stream) against 8 TB/s HBM peak;
+  cpu_baseline  the float64 CPU oracle timed on a bounded sample of the same
+             workload (a few sequences), as GB/s of algorithmic bytes.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+
+WORKLOADS = {
+    "llama3_70b": "Llama-3-70B-shaped GQA decode layer: 128 seqs, 64 query / 8 KV heads, d 128, "
+                  "bf16, block 16, lengths log-uniform [256, 8192]",
+    "llama2_7b": "Llama-2-7B-shaped MHA decode layer: 64 seqs, 32/32 heads, d 128, fp16, "
+                 "block 16, lengths uniform [128, 2048]",
+}
+
+
+def algorithmic_bytes(w):
+    """K+V read once per (sequence, KV head) plus Q: sum_s L_s*H_kv*d*2*e + S*H_q*d*e."""
+    e = 4 if w.dtype == 0 else 2
+    kv = int(np.sum(np.asarray(w.context_lens, dtype=np.int64))) * w.num_kv_heads * w.head_dim * 2 * e
+    q = w.num_seqs * w.num_q_heads * w.head_dim * e
+    return kv + q
+
+
+def make_workload(name):
+    from paged_kv_cache_442_amd import workloads as wl
+    return {"llama3_70b": wl.llama3_70b, "llama2_7b": wl.llama2_7b}[name]()
+
+
+def cpu_baseline(w, budget_s):
+    """Time the float64 oracle on whole sequences until ``budget_s`` is spent."""
+    from oracle import attention, fpbits
+    scale = attention.default_scale(w.head_dim)
+    e = 4 if w.dtype == 0 else 2
+    order = np.random.default_rng(0).permutation(w.num_seqs)
+    done, nbytes, t_total = [], 0, 0.0
+    for s in order:
+        t0 = time.perf_counter()
+        kt, vt = w.seq_tokens(int(s))
+        attention.contiguous_decode(w.dtype, w.q[s], fpbits.decode(w.dtype, kt),
+                                    fpbits.decode(w.dtype, vt), scale)
+        t_total += time.perf_counter() - t0
+        done.append(int(s))
+        nbytes += int(w.context_lens[s]) * w.num_kv_heads * w.head_dim * 2 * e + \
+            w.num_q_heads * w.head_dim * e
+        if t_total >= budget_s:
+            break
+    return {
+        "value": round(nbytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d of %d sequences (%d tokens), float64 numpy oracle, single thread, %.1f s"
+                  % (len(done), w.num_seqs, int(np.sum(np.asarray(w.context_lens)[done])), t_total),
+    }
+
+
+def copy_ceiling_gbps(torch, nbytes=1 << 30, reps=20):
+    """Read+write GB/s of a plain device-to-device copy (a measured ceiling)."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="llama3_70b")
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the CPU-oracle baseline (0 disables it)")
+    ap.add_argument("--no-copy-ceiling", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_442_amd import binding as pa
+    from paged_kv_cache_442_amd import workloads as wl
+    from paged_kv_cache_442_amd.session import DecodeSession
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pa.lib()  # fail loudly if the library is missing
+
+    t0 = time.perf_counter()
+    w = make_workload(args.workload)
+    print("[bench] workload %s drawn in %.1f s" % (args.workload, time.perf_counter() - t0),
+          file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    sess = DecodeSession(w, partition_tokens=args.partition)
+    print("[bench] cache written in %.1f s" % (time.perf_counter() - t0), file=sys.stderr, flush=True)
+
+    B = algorithmic_bytes(w)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        sess.step()
+    torch.cuda.synchronize()
+
+    n = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(n):
+        e = ev[i]
+        e[0].record(stream)
+        sess.write_new_tokens()
+        e[1].record(stream)
+        sess.decode_partitions()
+        e[2].record(stream)
+        sess.decode_reduce()
+        e[3].record(stream)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    ms_step = total_ms / n
+    write_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    part_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    red_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+
+    part_avg_s = float(part_ms.mean()) * 1e-3
+    achieved = B / part_avg_s / 1e9
+    value = B / (ms_step * 1e-3) / 1e9
+
+    # sampled parity against the oracle on the timed output
+    from oracle import attention, fpbits
+    got = sess.out.cpu().numpy().astype(np.float64)
+    lens = np.asarray(w.context_lens)
+    worst = 0.0
+    for s in sorted({int(np.argmin(lens)), int(np.argmax(lens))}):
+        kt, vt = w.seq_tokens(s)
+        want = attention.contiguous_decode(w.dtype, w.q[s], fpbits.decode(w.dtype, kt),
+                                           fpbits.decode(w.dtype, vt),
+                                           attention.default_scale(w.head_dim))
+        worst = max(worst, float(np.max(np.abs(got[s] - want))))
+
+    # host block manager: one appended token per sequence (A1), on a host-only pool
+    hp = pa.pa_alloc_pool(pa.make_desc(1, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                                       w.dtype), None, w.free_order)
+    hseqs = [pa.pa_seq_new(hp) for _ in range(w.num_seqs)]
+    for s, L in zip(hseqs, lens):
+        pa.pa_seq_append(hp, s, int(L) - 1)
+    t0 = time.perf_counter()
+    for s in hseqs:
+        pa.pa_seq_append(hp, s, 1)
+    host_mgr_us = (time.perf_counter() - t0) * 1e6
+
+    blocks = sum(-(-int(L) // w.block_size) for L in lens)
+    waste = 1.0 - float(lens.sum()) / (blocks * w.block_size)
+
+    ceiling = None if args.no_copy_ceiling else copy_ceiling_gbps(torch)
+    cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+
+    line = {
+        "metric": "paged-decode KV GB/s and % of HBM peak at 1 MI355X; tokens/sec per layer",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == wl.BF16 else ("f16" if w.dtype == wl.F16 else "f32"),
+        "data": "synthetic (seeded N(0,1) K/V/Q, seeded block permutation)",
+        "config": {
+            "workload": args.workload,
+            "description": WORKLOADS[args.workload],
+            "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "num_blocks": w.num_blocks,
+            "total_context_tokens": int(lens.sum()), "max_context": int(lens.max()),
+            "partition_tokens": args.partition or 512,
+            "algorithmic_bytes_per_step": B,
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "kernel_ms": {"reshape_and_cache": round(float(write_ms.mean()), 5),
+                      "decode_partitions": round(float(part_ms.mean()), 5),
+                      "decode_reduce": round(float(red_ms.mean()), 5)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_partition_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "copy_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+        "max_abs_err_sampled": worst,
+        "internal_waste_pct": round(100 * waste, 3),
+        "host_manager_us_per_step": round(host_mgr_us, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

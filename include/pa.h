@@ -163,7 +163,7 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
  *   "vLLM explained", two implementation layers: same result as ordinary attention).
  *
  * The work is split over partitions of `partition_tokens` consecutive tokens (0 =
- * default 512; else a positive multiple of 64): one pass computes each partition's
+ * default 512; else a positive multiple of 64, at most 4096): one pass computes each partition's
  * softmax statistics and normalized output (pa_decode_partitions), a second pass
  * merges the partitions of each sequence with log-sum-exp weights (pa_decode_reduce).
  * Sequences that fit one partition are finished by the first pass.  pa_decode runs

@@ -119,9 +119,10 @@ int prepare_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs
     return fail(PA_E_UNSUPPORTED, "block_size %d (must be a multiple of %d)", d.block_size,
                 pa::kTileTokens);
   if (partition_tokens == 0) partition_tokens = pa::kDefaultPartition;
-  if (partition_tokens < 0 || partition_tokens % (pa::kTileTokens * pa::kDecodeWaves) != 0)
-    return fail(PA_E_INVAL, "partition_tokens %d must be a positive multiple of %d", partition_tokens,
-                pa::kTileTokens * pa::kDecodeWaves);
+  if (partition_tokens < 0 || partition_tokens % (pa::kTileTokens * pa::kDecodeWaves) != 0 ||
+      partition_tokens > pa::kMaxPartition)
+    return fail(PA_E_INVAL, "partition_tokens %d must be a positive multiple of %d, at most %d",
+                partition_tokens, pa::kTileTokens * pa::kDecodeWaves, pa::kMaxPartition);
   if (!std::isfinite(scale)) return fail(PA_E_INVAL, "scale is not finite");
   if (num_seqs == 0) {
     call->args = pa::DecodeArgs{};

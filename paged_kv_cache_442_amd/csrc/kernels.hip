@@ -28,6 +28,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // overflow, and the common path skips the rescale entirely.
 constexpr float kRescaleSlack = 8.0f;
 
+// s_waitcnt immediate for "vmcnt(0)" with expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // ------------------------------------------------------------------ element formats
 // Each format says how one dword of q meets one dword of k (fp32-accumulated dot
 // product) and how a dword of v widens to fp32.
@@ -187,11 +190,24 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, 2) void decode_partition_kern
   const int64_t row_bytes = kHeadDim * E::kBytes;
   const int64_t run_bytes = static_cast<int64_t>(a.block_size) * row_bytes;
 
+  // Block ids of this wave's tiles (wave, wave + 4, ...), one per lane, loaded once
+  // per partition; each tile takes its id with readlane, so no memory wait stands
+  // between one tile's loads and the next.  Entries past the sequence's last block
+  // are not read.  (partition_tokens <= 4096 keeps a wave's tiles within 64 lanes.)
+  int tbl_lane = 0;
+  {
+    const int j = wave + kDecodeWaves * lane;
+    if (j < n_tiles) tbl_lane = tbl[(t_begin + j * kTileTokens) / a.block_size];
+  }
+  // Wait for it here, before any K/V load is in flight: otherwise the compiler
+  // cannot prove inside the tile loop that it has landed and drains every
+  // outstanding load on each tile.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
   auto tile_offset = [&](int j) -> int64_t {
     const int t0 = t_begin + j * kTileTokens;
-    const int lb = t0 / a.block_size;
-    const int off = t0 - lb * a.block_size;
-    int phys = tbl[lb];
+    const int off = t0 % a.block_size;
+    int phys = __builtin_amdgcn_readlane(tbl_lane, (j - wave) / kDecodeWaves);
     if (static_cast<unsigned>(phys) >= static_cast<unsigned>(a.num_blocks)) {
       bad_blk = true;
       phys = 0;
@@ -205,19 +221,20 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, 2) void decode_partition_kern
     for (int i = 0; i < LOADS; ++i) r[i] = src[i * kWave];
   };
 
-  // Tile j's K and V rows are in kr / vr on entry; tile jn's (if jn < n_tiles) are
-  // on their way into the same registers on exit: K as soon as tile j's K is in
-  // LDS, V as soon as tile j's PV has consumed it.
-  auto process = [&](int j, int jn, u32x4 (&kr)[LOADS], u32x4 (&vr)[LOADS]) {
+  // Tile j's K and V rows are in kr / vr on entry; tile jn's are on their way into
+  // the same registers on exit: K as soon as tile j's K is in LDS, V as soon as tile
+  // j's PV has consumed it.  Past the last tile the loads repeat tile j (cache hits)
+  // so that the count of loads in flight, and with it every wait, is the same on
+  // each pass.
+  auto process = [&](int j, int jn, int64_t cur_off, u32x4 (&kr)[LOADS], u32x4 (&vr)[LOADS]) {
     const int t0 = t_begin + j * kTileTokens;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int r = i * TG + tg;
       lds.main.k[wave][r][ch] = kr[i];
     }
-    const bool more = jn < n_tiles;
-    const int64_t next_off = more ? tile_offset(jn) : 0;
-    if (more) load_rows(kbase, next_off, kr);
+    const int64_t next_off = jn < n_tiles ? tile_offset(jn) : cur_off;
+    load_rows(kbase, next_off, kr);
     wave_sync();
 
     // QK, software-pipelined by hand: the K chunks of all NPL rows are read
@@ -337,18 +354,19 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, 2) void decode_partition_kern
 #pragma unroll
         for (int e = 0; e < VD; ++e) o[h][e] = fmaf(pv[h], v[e], o[h][e]);
     }
-    if (more) load_rows(vbase, next_off, vr);
+    load_rows(vbase, next_off, vr);
     wave_sync();
+    return next_off;
   };
 
   {
     u32x4 kr[LOADS], vr[LOADS];
     if (wave < n_tiles) {
-      const int64_t off = tile_offset(wave);
+      int64_t off = tile_offset(wave);
       load_rows(kbase, off, kr);
       load_rows(vbase, off, vr);
+      for (int j = wave; j < n_tiles; j += kDecodeWaves) off = process(j, j + kDecodeWaves, off, kr, vr);
     }
-    for (int j = wave; j < n_tiles; j += kDecodeWaves) process(j, j + kDecodeWaves, kr, vr);
   }
 
   // ---- merge the waves

@@ -13,6 +13,7 @@ constexpr int kHeadDim = 128;        // head_dim the attention kernels are built
 constexpr int kTileTokens = 16;      // tokens per K/V tile streamed by the decode kernel
 constexpr int kDecodeWaves = 4;      // waves per decode workgroup
 constexpr int kDefaultPartition = 512;
+constexpr int kMaxPartition = kDecodeWaves * 64 * kTileTokens;  // a wave's tiles fit one wave of lanes
 
 struct DecodeArgs {
   const void* q;            // [S][Hq][128]
