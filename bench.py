@@ -133,7 +133,7 @@ def main():
     torch.cuda.synchronize()
 
     n = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -143,17 +143,20 @@ def main():
         e[0].record(stream)
         sess.write_new_tokens()
         e[1].record(stream)
-        sess.decode_partitions()
+        sess.decode_plan()
         e[2].record(stream)
-        sess.decode_reduce()
+        sess.decode_partitions()
         e[3].record(stream)
+        sess.decode_reduce()
+        e[4].record(stream)
     t_stop.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_stop)
     ms_step = total_ms / n
     write_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    part_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    red_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    plan_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    part_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    red_ms = np.array([e[3].elapsed_time(e[4]) for e in ev])
 
     part_avg_s = float(part_ms.mean()) * 1e-3
     achieved = B / part_avg_s / 1e9
@@ -213,6 +216,7 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
         "kernel_ms": {"reshape_and_cache": round(float(write_ms.mean()), 5),
+                      "decode_plan": round(float(plan_ms.mean()), 5),
                       "decode_partitions": round(float(part_ms.mean()), 5),
                       "decode_reduce": round(float(red_ms.mean()), 5)},
         "roofline": {

@@ -163,12 +163,19 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
  *   "vLLM explained", two implementation layers: same result as ordinary attention).
  *
  * The work is split over partitions of `partition_tokens` consecutive tokens (0 =
- * default 512; else a positive multiple of 64, at most 4096): one pass computes each partition's
- * softmax statistics and normalized output (pa_decode_partitions), a second pass
- * merges the partitions of each sequence with log-sum-exp weights (pa_decode_reduce).
- * Sequences that fit one partition are finished by the first pass.  pa_decode runs
- * both.  The result does not depend on which physical blocks hold the data: the
- * summation order follows logical token order only.
+ * default 512; else a positive multiple of 64, at most 4096), run as three kernels
+ * on `stream`:
+ *   pa_decode_plan        lists the (sequence, partition) work items in the workspace
+ *                         and zeroes its work counter;
+ *   pa_decode_partitions  persistent workgroups draw items from that counter and
+ *                         compute each partition's softmax statistics and normalized
+ *                         output; sequences that fit one partition are finished here;
+ *   pa_decode_reduce      merges each longer sequence's partitions with log-sum-exp
+ *                         weights.
+ * pa_decode runs all three.  pa_decode_partitions needs a pa_decode_plan with the same
+ * arguments earlier on the stream, and pa_decode_reduce needs both.  The result does
+ * not depend on which physical blocks hold the data: the summation order follows
+ * logical token order only.  Calls that share one workspace must not overlap.
  *
  *   q            device [num_seqs][num_q_heads][head_dim], pool dtype, contiguous
  *   block_tables device int32 [num_seqs][max_blocks]; entries past a sequence's last
@@ -178,14 +185,20 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
  *   scale        softmax scale, usually 1/sqrt(head_dim)
  *   out          device fp32 [num_seqs][num_q_heads][head_dim]; an empty sequence
  *                gets zeros
- *   workspace    device scratch of at least pa_decode_workspace_bytes(...) bytes
- *                (partition partials); its contents need no initialization
+ *   workspace    device scratch of at least pa_decode_workspace_bytes(...) bytes,
+ *                16-byte aligned (work list, counter and partition partials); its
+ *                contents need no initialization
  * A sequence whose length exceeds max_context or max_blocks * block_size, or whose
  * table holds an id outside [0, num_blocks), gets NaN outputs; nothing outside the
  * pool is read.  Supported: head_dim 128; num_q_heads / num_kv_heads in {1, 2, 4, 8,
  * 16}; any block_size that is a multiple of 16; all three dtypes (fp32 accumulation). */
 int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context, int32_t partition_tokens);
+int pa_decode_plan(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
+                   int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                   const int32_t* context_lens, int32_t max_context, float scale,
+                   int32_t partition_tokens, float* out, void* workspace, int64_t workspace_bytes,
+                   void* stream);
 int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
               int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
               const int32_t* context_lens, int32_t max_context, float scale,

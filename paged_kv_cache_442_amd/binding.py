@@ -59,6 +59,7 @@ _SIGNATURES = {
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, _I32, _P]),
     "pa_decode_workspace_bytes": (_I64, [_P, _I32, _I32, _I32, _I32]),
     "pa_decode": (ctypes.c_int, _DECODE_ARGS),
+    "pa_decode_plan": (ctypes.c_int, _DECODE_ARGS),
     "pa_decode_partitions": (ctypes.c_int, _DECODE_ARGS),
     "pa_decode_reduce": (ctypes.c_int, _DECODE_ARGS),
     "pa_last_error": (ctypes.c_char_p, []),
@@ -283,6 +284,12 @@ def pa_decode(pool, layer, q, block_tables, context_lens, max_context, scale, ou
     """q: GPU ``[S][H_q][d]`` pool dtype; out: GPU fp32 ``[S][H_q][d]``."""
     _decode(lib().pa_decode, pool, layer, q, block_tables, context_lens, max_context, scale, out,
             workspace, partition_tokens, stream)
+
+
+def pa_decode_plan(pool, layer, q, block_tables, context_lens, max_context, scale, out, workspace,
+                   partition_tokens=0, stream=None):
+    _decode(lib().pa_decode_plan, pool, layer, q, block_tables, context_lens, max_context, scale,
+            out, workspace, partition_tokens, stream)
 
 
 def pa_decode_partitions(pool, layer, q, block_tables, context_lens, max_context, scale, out,

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -91,6 +92,13 @@ int check_device_pool(const pa_pool* p, int32_t layer) {
   return PA_OK;
 }
 
+// Workspace: [work header | work items | partition outputs | partition log-sum-exps].
+constexpr int64_t kWorkHeaderBytes = 256;
+
+int64_t items_bytes(int64_t num_seqs, int64_t pmax) {
+  return (num_seqs * pmax * 8 + 255) / 256 * 256;
+}
+
 struct DecodeCall {
   pa::DecodeArgs args;
   int group;
@@ -135,9 +143,8 @@ int prepare_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs
   if (num_seqs > 0x7fffffff / num_q_heads) return fail(PA_E_RANGE, "num_seqs * num_q_heads overflows");
   const int64_t pmax = std::max<int64_t>(1, (static_cast<int64_t>(max_context) + partition_tokens - 1) /
                                                 partition_tokens);
-  if (pmax > 65535) return fail(PA_E_RANGE, "max_context %d needs %lld partitions (limit 65535)",
-                                max_context, static_cast<long long>(pmax));
-  if (d.num_kv_heads > 65535) return fail(PA_E_UNSUPPORTED, "more than 65535 KV heads");
+  if (static_cast<int64_t>(num_seqs) * pmax * d.num_kv_heads > 0x7fffffff)
+    return fail(PA_E_RANGE, "num_seqs * partitions * num_kv_heads exceeds 2^31 - 1");
   const int64_t need = pa_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_context,
                                                  partition_tokens);
   if (need < 0) return static_cast<int>(need);
@@ -156,8 +163,11 @@ int prepare_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs
   a.ctx = context_lens;
   a.out = out;
   const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_lse = a.part_o ? a.part_o + rows * pmax * pa::kHeadDim : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.work_header = reinterpret_cast<int32_t*>(ws);
+  a.work_items = reinterpret_cast<int32_t*>(ws + kWorkHeaderBytes);
+  a.part_o = reinterpret_cast<float*>(ws + kWorkHeaderBytes + items_bytes(num_seqs, pmax));
+  a.part_lse = a.part_o + rows * pmax * pa::kHeadDim;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = d.num_kv_heads;
@@ -375,11 +385,28 @@ int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t
   if (num_seqs < 0 || num_q_heads < 0 || max_context < 0 || partition_tokens < 0)
     return fail(PA_E_INVAL, "negative size");
   if (partition_tokens == 0) partition_tokens = pa::kDefaultPartition;
-  const int64_t pmax = (static_cast<int64_t>(max_context) + partition_tokens - 1) / partition_tokens;
-  if (pmax <= 1) return 0;  // every sequence fits one partition: no partials
-  const __int128 b = static_cast<__int128>(num_seqs) * num_q_heads * pmax * (pa::kHeadDim + 1) * 4;
+  const int64_t pmax =
+      std::max<int64_t>(1, (static_cast<int64_t>(max_context) + partition_tokens - 1) / partition_tokens);
+  // Partials are needed only when a sequence can span more than one partition.
+  const __int128 partials =
+      pmax > 1 ? static_cast<__int128>(num_seqs) * num_q_heads * pmax * (pa::kHeadDim + 1) * 4 : 0;
+  const __int128 b = kWorkHeaderBytes + items_bytes(num_seqs, pmax) + partials;
   if (b > std::numeric_limits<int64_t>::max()) return fail(PA_E_RANGE, "workspace size overflows");
   return static_cast<int64_t>(b);
+}
+
+int pa_decode_plan(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
+                   int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                   const int32_t* context_lens, int32_t max_context, float scale,
+                   int32_t partition_tokens, float* out, void* workspace, int64_t workspace_bytes,
+                   void* stream) {
+  DecodeCall c;
+  int st = prepare_decode(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+                          context_lens, max_context, scale, partition_tokens, out, workspace,
+                          workspace_bytes, &c);
+  if (st) return st;
+  if (c.args.num_seqs == 0) return ok();
+  return hip_status(pa::launch_decode_plan(c.args, static_cast<hipStream_t>(stream)), "pa_decode_plan");
 }
 
 int pa_decode_partitions(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
@@ -417,7 +444,11 @@ int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs, int
               const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
               int32_t max_context, float scale, int32_t partition_tokens, float* out,
               void* workspace, int64_t workspace_bytes, void* stream) {
-  int st = pa_decode_partitions(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+  int st = pa_decode_plan(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+                          context_lens, max_context, scale, partition_tokens, out, workspace,
+                          workspace_bytes, stream);
+  if (st) return st;
+  st = pa_decode_partitions(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
                                 context_lens, max_context, scale, partition_tokens, out, workspace,
                                 workspace_bytes, stream);
   if (st) return st;

@@ -10,6 +10,8 @@
 // on the vector ALUs, not on MFMA.
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace pa {
@@ -112,9 +114,31 @@ __device__ __forceinline__ float dpp_xor_add(float x) {
 // partition writes `out`, otherwise the partition writes its normalized o and its
 // base-2 log-sum-exp for the reduce kernel.
 template <class E, int G>
-__global__ __launch_bounds__(kWave * kDecodeWaves, 2) void decode_partition_kernel(const DecodeArgs a) {
-  constexpr int NCH = kHeadDim * E::kBytes / 16;  // 16-byte chunks per K/V row
-  constexpr int TG = kWave / NCH;                 // rows per wave-wide 16-byte load
+struct DecodeLds {
+  static constexpr int NCH = kHeadDim * E::kBytes / 16;  // 16-byte chunks per K/V row
+  static constexpr int TG = kWave / NCH;                 // rows per wave-wide 16-byte load
+  struct Main {
+    u32x4 k[kDecodeWaves][kTileTokens][NCH + 1];  // +1: row padding against bank conflicts
+    float p[kDecodeWaves][kTileTokens][G];
+  };
+  struct Merge {
+    float o[kDecodeWaves][TG][G][kHeadDim];
+  };
+  union {
+    Main main;
+    Merge merge;
+  };
+  float m[kDecodeWaves][G];
+  float l[kDecodeWaves][G];
+};
+
+// One work item: (sequence, KV head, partition).  Every thread of the workgroup calls
+// this with the same item.
+template <class E, int G>
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeLds<E, G>& lds, int seq,
+                                            int kvh, int part) {
+  constexpr int NCH = DecodeLds<E, G>::NCH;
+  constexpr int TG = DecodeLds<E, G>::TG;
   constexpr int LOADS = kTileTokens / TG;         // 16-byte loads per lane per tile (K, and V)
   constexpr int VD = 16 / E::kBytes;              // elements per 16-byte chunk
   constexpr int LPP = G >= 4 ? 1 : 4 / G;         // lanes sharing one (head, token) dot product
@@ -122,40 +146,19 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, 2) void decode_partition_kern
   constexpr int TSTRIDE = kWave / (LPP * G);      // token distance between a lane's pairs
   constexpr int QCH = NCH / LPP;                  // 16-byte chunks of q per lane
 
-  struct MainLds {
-    u32x4 k[kDecodeWaves][kTileTokens][NCH + 1];  // +1: row padding against bank conflicts
-    float p[kDecodeWaves][kTileTokens][G];
-  };
-  struct MergeLds {
-    float o[kDecodeWaves][TG][G][kHeadDim];
-  };
-  union Lds {
-    MainLds main;
-    MergeLds merge;
-  };
-  __shared__ Lds lds;
-  __shared__ float s_m[kDecodeWaves][G];
-  __shared__ float s_l[kDecodeWaves][G];
-
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int seq = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int part = blockIdx.z;
   const int Hq = a.num_q_heads;
   const int L = a.ctx[seq];
   const bool bad_len = L < 0 || L > a.max_context ||
                        static_cast<int64_t>(L) > static_cast<int64_t>(a.max_blocks) * a.block_size;
   const size_t group_row = static_cast<size_t>(seq) * Hq + static_cast<size_t>(kvh) * G;
   if (bad_len || L == 0) {
-    if (part == 0) {
-      const float fill = bad_len ? __builtin_nanf("") : 0.0f;
-      for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x) a.out[group_row * kHeadDim + i] = fill;
-    }
+    const float fill = bad_len ? __builtin_nanf("") : 0.0f;
+    for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x) a.out[group_row * kHeadDim + i] = fill;
     return;
   }
   const int t_begin = part * a.partition_tokens;
-  if (t_begin >= L) return;
   const int t_end = min(L, t_begin + a.partition_tokens);
   const int n_tiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
   const int n_parts = (L + a.partition_tokens - 1) / a.partition_tokens;
@@ -375,8 +378,8 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, 2) void decode_partition_kern
   for (int m = LPP * G; m < kWave; m <<= 1) l_acc += __shfl_xor(l_acc, m);
   __syncthreads();  // every wave is done with lds.main before lds.merge overwrites it
   if (tq == 0 && sub == 0) {
-    s_l[wave][hq] = l_acc;
-    s_m[wave][hq] = m_mine;
+    lds.l[wave][hq] = l_acc;
+    lds.m[wave][hq] = m_mine;
   }
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -391,13 +394,13 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, 2) void decode_partition_kern
     const int d4 = (idx % (kHeadDim / 4)) * 4;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, lds.m[w][h]);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     float lt = 0.0f;
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) {
-      const float W = __builtin_amdgcn_exp2f(s_m[w][h] - M);
-      lt += W * s_l[w][h];
+      const float W = __builtin_amdgcn_exp2f(lds.m[w][h] - M);
+      lt += W * lds.l[w][h];
       f32x4 sum = *reinterpret_cast<const f32x4*>(&lds.merge.o[w][0][h][d4]);
 #pragma unroll
       for (int g = 1; g < TG; ++g) sum += *reinterpret_cast<const f32x4*>(&lds.merge.o[w][g][h][d4]);
@@ -412,6 +415,107 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, 2) void decode_partition_kern
       *reinterpret_cast<f32x4*>(a.part_o + prow * kHeadDim + d4) = res;
       if (d4 == 0) a.part_lse[prow] = M + __log2f(lt);
     }
+  }
+}
+
+// Persistent decode workgroups: each takes (item, KV head) work numbers from the
+// counter the plan kernel zeroed, until the numbers run out; the next number is
+// fetched while the current item runs.
+template <class E, int G>
+__global__ __launch_bounds__(kWave * kDecodeWaves, 2) void decode_partition_kernel(const DecodeArgs a) {
+  __shared__ DecodeLds<E, G> lds;
+  __shared__ int s_next;
+  int* counter = a.work_header;
+  const int n_work = a.work_header[1];
+  if (threadIdx.x == 0) s_next = atomicAdd(counter, 1);
+  __syncthreads();
+  int work = s_next;
+  while (work < n_work) {
+    __syncthreads();  // s_next has been read and the previous item's LDS is free
+    if (threadIdx.x == 0) s_next = atomicAdd(counter, 1);
+    const int item = work / a.num_kv_heads;
+    decode_item<E, G>(a, lds, a.work_items[2 * item], work - item * a.num_kv_heads,
+                      a.work_items[2 * item + 1]);
+    __syncthreads();
+    work = s_next;
+  }
+}
+
+// ------------------------------------------------------------------ decode plan
+// One workgroup lists the work: every full partition of every sequence, then each
+// sequence's last partial partition (so that the smallest items are taken last),
+// and a single item for an empty or invalid sequence (it writes the zeros or NaNs).
+// It also zeroes the work counter the persistent decode kernel draws from.
+__device__ __forceinline__ int block_exclusive_scan(int x, int* s_tmp, int* total) {
+  // s_tmp: kPlanThreads / 64 ints
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_tmp[wv] = incl;
+  __syncthreads();
+  int base = 0, sum = 0;
+  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) {
+    const int t = s_tmp[w];
+    if (w < wv) base += t;
+    sum += t;
+  }
+  __syncthreads();
+  *total = sum;
+  return base + incl - x;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeArgs a) {
+  __shared__ int s_tmp[kPlanThreads / 64];
+  const int P = a.partition_tokens;
+  auto classify = [&](int s, int* full, int* partial) {
+    const int L = a.ctx[s];
+    const bool bad = L < 0 || L > a.max_context ||
+                     static_cast<int64_t>(L) > static_cast<int64_t>(a.max_blocks) * a.block_size;
+    if (bad || L == 0) {
+      *full = 0;
+      *partial = 1;
+    } else {
+      *full = L / P;
+      *partial = (L % P) != 0;
+    }
+  };
+  // Pass 1: the number of full items (the partial items are listed after them).
+  int full_total = 0;
+  for (int s0 = 0; s0 < a.num_seqs; s0 += blockDim.x) {
+    const int s = s0 + threadIdx.x;
+    int f = 0, pp = 0;
+    if (s < a.num_seqs) classify(s, &f, &pp);
+    int t;
+    block_exclusive_scan(f, s_tmp, &t);
+    full_total += t;
+  }
+  // Pass 2: positions, then the items themselves.
+  int full_base = 0, part_base = full_total;
+  for (int s0 = 0; s0 < a.num_seqs; s0 += blockDim.x) {
+    const int s = s0 + threadIdx.x;
+    int f = 0, pp = 0;
+    if (s < a.num_seqs) classify(s, &f, &pp);
+    int tf, tp;
+    const int fo = block_exclusive_scan(f, s_tmp, &tf) + full_base;
+    const int po = block_exclusive_scan(pp, s_tmp, &tp) + part_base;
+    for (int k = 0; k < f; ++k) {
+      a.work_items[2 * (fo + k)] = s;
+      a.work_items[2 * (fo + k) + 1] = k;
+    }
+    if (pp) {
+      a.work_items[2 * po] = s;
+      a.work_items[2 * po + 1] = f;
+    }
+    full_base += tf;
+    part_base += tp;
+  }
+  if (threadIdx.x == 0) {
+    a.work_header[0] = 0;
+    a.work_header[1] = part_base * a.num_kv_heads;
   }
 }
 
@@ -502,18 +606,39 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* __restr
   for (; c < block_chunks; c += 256) d[c] = s[c];
 }
 
+template <class E, int G>
+hipError_t launch_persistent(const DecodeArgs& a, hipStream_t s) {
+  // Workgroups resident at once on the current device (cached per device).
+  static int cached[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partition_kernel<E, G>,
+                                                     kWave * kDecodeWaves, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cached[dev] = std::max(1, per_cu) * std::max(1, cus);
+  }
+  const int64_t upper = static_cast<int64_t>(a.num_seqs) * a.pmax * a.num_kv_heads;
+  const int grid = static_cast<int>(std::min<int64_t>(cached[dev], upper));
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_partition_kernel<E, G>), dim3(grid),
+                     dim3(kWave * kDecodeWaves), 0, s, a);
+  return hipGetLastError();
+}
+
 template <class E>
 hipError_t launch_decode_typed(const DecodeArgs& a, int group, hipStream_t s) {
-  const dim3 grid(a.num_seqs, a.num_kv_heads, a.pmax);
-  const dim3 block(kWave * kDecodeWaves);
   switch (group) {
-    case 1: hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_partition_kernel<E, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_partition_kernel<E, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_partition_kernel<E, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_partition_kernel<E, 8>), grid, block, 0, s, a); break;
+    case 1: return launch_persistent<E, 1>(a, s);
+    case 2: return launch_persistent<E, 2>(a, s);
+    case 4: return launch_persistent<E, 4>(a, s);
+    case 8: return launch_persistent<E, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -526,6 +651,12 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int dtype, int group, h
     case 2: return launch_decode_typed<ElemBF16>(a, group, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_decode_plan(const DecodeArgs& a, hipStream_t s) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t s) {

@@ -13,6 +13,7 @@ constexpr int kHeadDim = 128;        // head_dim the attention kernels are built
 constexpr int kTileTokens = 16;      // tokens per K/V tile streamed by the decode kernel
 constexpr int kDecodeWaves = 4;      // waves per decode workgroup
 constexpr int kDefaultPartition = 512;
+constexpr int kPlanThreads = 1024;
 constexpr int kMaxPartition = kDecodeWaves * 64 * kTileTokens;  // a wave's tiles fit one wave of lanes
 
 struct DecodeArgs {
@@ -24,11 +25,16 @@ struct DecodeArgs {
   float* out;               // [S][Hq][128]
   float* part_o;            // [S][Hq][pmax][128]
   float* part_lse;          // [S][Hq][pmax], base-2 log-sum-exp of scaled scores
+  int32_t* work_header;     // [0] work counter, [1] number of (item, KV head) work units
+  int32_t* work_items;      // [S * pmax][2] (sequence, partition)
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks, num_blocks, block_size;
   int32_t max_context, partition_tokens, pmax;
   float scale_log2;         // scale * log2(e)
 };
 
+// The plan kernel lists the work items and zeroes the work counter; the partition
+// kernel (persistent) needs a plan on the same workspace before it.
+hipError_t launch_decode_plan(const DecodeArgs& a, hipStream_t s);
 // dtype: 0 fp32, 1 fp16, 2 bf16; group = num_q_heads / num_kv_heads in {1, 2, 4, 8}.
 hipError_t launch_decode_partitions(const DecodeArgs& a, int dtype, int group, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t s);

@@ -93,7 +93,7 @@ class DecodeSession:
         self.out = torch.empty(S, w.num_q_heads, w.head_dim, dtype=torch.float32, device=device)
         ws = pa.pa_decode_workspace_bytes(self.pool, S, w.num_q_heads, self.max_context,
                                           partition_tokens)
-        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device) if ws else None
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
         self.scale = 1.0 / math.sqrt(w.head_dim)
 
     # ---------------------------------------------------------------- one decode step
@@ -104,6 +104,10 @@ class DecodeSession:
     def decode(self, stream=None):
         pa.pa_decode(self.pool, self.layer, self.q, self.tables, self.ctx, self.max_context,
                      self.scale, self.out, self.workspace, self.partition_tokens, stream)
+
+    def decode_plan(self, stream=None):
+        pa.pa_decode_plan(self.pool, self.layer, self.q, self.tables, self.ctx, self.max_context,
+                          self.scale, self.out, self.workspace, self.partition_tokens, stream)
 
     def decode_partitions(self, stream=None):
         pa.pa_decode_partitions(self.pool, self.layer, self.q, self.tables, self.ctx,

@@ -125,13 +125,14 @@ def test_physical_placement_does_not_change_bits():
     assert torch.equal(shuffled.out.view(torch.int32), ident.out.view(torch.int32))
 
 
-def test_partitions_then_reduce_equals_decode():
-    announce("partitions + reduce == decode")
+def test_plan_partitions_reduce_equals_decode():
+    announce("plan + partitions + reduce == decode")
     w = wl.custom_decode(8, wl.BF16, [1000, 3, 512, 513], 8, 1, block_size=16)
     sess = DecodeSession(w, partition_tokens=64)
     sess.step()
     one = sess.out.clone()
     sess.out.zero_()
+    sess.decode_plan()
     sess.decode_partitions()
     sess.decode_reduce()
     torch.cuda.synchronize()
