@@ -40,6 +40,30 @@ def algorithmic_bytes(w):
     return kv + q
 
 
+def counter_traffic(root):
+    """HBM bytes per launch of the partition kernel from the committed rocprofv3 counters.
+
+    The counters (FETCH_SIZE, WRITE_SIZE in KiB per dispatch, each scaled by what the
+    same counter reads for a plain copy of known size) hold only for the kernel source
+    they were taken on: if its fingerprint differs, the figure is stale and None is
+    returned.
+    """
+    import hashlib
+    path = os.path.join(root, "profiles", "decode_partition_kernel_llama3_70b.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for name in rec["source_files"]:
+        with open(os.path.join(root, name), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return int(round(rec["fetch_kib_per_launch"] * 1024 * rec["fetch_scale"] +
+                     rec["write_kib_per_launch"] * 1024 * rec["write_scale"]))
+
+
 def make_workload(name):
     from paged_kv_cache_442_amd import workloads as wl
     return {"llama3_70b": wl.llama3_70b, "llama2_7b": wl.llama2_7b}[name]()
@@ -226,7 +250,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": counter_traffic(os.path.dirname(os.path.abspath(__file__)))
+            if args.workload == "llama3_70b" else None,
         },
         "copy_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
         "max_abs_err_sampled": worst,

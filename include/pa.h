@@ -190,8 +190,8 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
  *                contents need no initialization
  * A sequence whose length exceeds max_context or max_blocks * block_size, or whose
  * table holds an id outside [0, num_blocks), gets NaN outputs; nothing outside the
- * pool is read.  Supported: head_dim 128; num_q_heads / num_kv_heads in {1, 2, 4, 8,
- * 16}; any block_size that is a multiple of 16; all three dtypes (fp32 accumulation). */
+ * pool is read.  Supported: head_dim 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
+ * any block_size that is a multiple of 16; all three dtypes (fp32 accumulation). */
 int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context, int32_t partition_tokens);
 int pa_decode_plan(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
