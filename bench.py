@@ -64,8 +64,10 @@ def counter_traffic(root):
                      rec["write_kib_per_launch"] * 1024 * rec["write_scale"]))
 
 
-def make_workload(name):
+def make_workload(name, num_q_heads=None, fixed_len=0):
     from paged_kv_cache_442_amd import workloads as wl
+    if name == "llama3_70b" and (num_q_heads or fixed_len):
+        return wl.llama3_70b(num_q_heads=num_q_heads or 64, fixed_len=fixed_len)
     return {"llama3_70b": wl.llama3_70b, "llama2_7b": wl.llama2_7b}[name]()
 
 
@@ -115,6 +117,23 @@ def copy_ceiling_gbps(torch, nbytes=1 << 30, reps=20):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def read_ceiling_gbps(torch, nbytes=1 << 30, reps=20):
+    """Read-only GB/s of a plain device reduction over ``nbytes`` (a measured ceiling)."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        a.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        a.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +144,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline (0 disables it)")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--num-q-heads", type=int, default=0,
+                    help="diagnostic: query heads of the llama3_70b shape (default 64)")
+    ap.add_argument("--fixed-len", type=int, default=0,
+                    help="diagnostic: every llama3_70b sequence this many tokens long")
+    ap.add_argument("--contiguous-blocks", action="store_true",
+                    help="hand out blocks in order 0, 1, 2, ... (a diagnostic: no scattering)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -143,7 +168,9 @@ def main():
     pa.lib()  # fail loudly if the library is missing
 
     t0 = time.perf_counter()
-    w = make_workload(args.workload)
+    w = make_workload(args.workload, args.num_q_heads, args.fixed_len)
+    if args.contiguous_blocks:
+        w.free_order = np.arange(w.num_blocks, dtype=np.int32)
     print("[bench] workload %s drawn in %.1f s" % (args.workload, time.perf_counter() - t0),
           file=sys.stderr, flush=True)
     t0 = time.perf_counter()
@@ -213,6 +240,7 @@ def main():
     waste = 1.0 - float(lens.sum()) / (blocks * w.block_size)
 
     ceiling = None if args.no_copy_ceiling else copy_ceiling_gbps(torch)
+    rceiling = None if args.no_copy_ceiling else read_ceiling_gbps(torch)
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
     line = {
@@ -235,6 +263,7 @@ def main():
             "head_dim": w.head_dim, "block_size": w.block_size, "num_blocks": w.num_blocks,
             "total_context_tokens": int(lens.sum()), "max_context": int(lens.max()),
             "partition_tokens": args.partition or 512,
+            "block_placement": "contiguous" if args.contiguous_blocks else "seeded permutation",
             "algorithmic_bytes_per_step": B,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
@@ -254,6 +283,7 @@ def main():
             if args.workload == "llama3_70b" else None,
         },
         "copy_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+        "read_ceiling_GBps": None if rceiling is None else round(rceiling, 1),
         "max_abs_err_sampled": worst,
         "internal_waste_pct": round(100 * waste, 3),
         "host_manager_us_per_step": round(host_mgr_us, 1),

@@ -15,7 +15,9 @@ F32, F16, BF16 = 0, 1, 2
 
 PA_OK, PA_E_INVAL, PA_E_NOMEM, PA_E_HIP, PA_E_UNSUPPORTED, PA_E_RANGE = 0, -1, -2, -3, -4, -5
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+# PA_LIB_PATH selects another build of the same library (the default is the in-tree one).
+LIB_PATH = os.environ.get("PA_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libpa.so")
 
 _lib = None
 

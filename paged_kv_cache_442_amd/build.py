@@ -23,6 +23,9 @@ HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
+    # A single-lane atomic stays a single-lane atomic (the wave-aggregating rewrite
+    # needs the result at once, which would stall the decode kernel's load pipeline).
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 

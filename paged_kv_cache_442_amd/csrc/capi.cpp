@@ -96,7 +96,7 @@ int check_device_pool(const pa_pool* p, int32_t layer) {
 constexpr int64_t kWorkHeaderBytes = 256;
 
 int64_t items_bytes(int64_t num_seqs, int64_t pmax) {
-  return (num_seqs * pmax * 8 + 255) / 256 * 256;
+  return (num_seqs * pmax * 16 + 255) / 256 * 256;
 }
 
 struct DecodeCall {

@@ -41,6 +41,7 @@ struct ElemF32 {
   __device__ static float dot(uint32_t q, uint32_t k, float acc) {
     return fmaf(__uint_as_float(q), __uint_as_float(k), acc);
   }
+  __device__ static float dot0(uint32_t q, uint32_t k) { return __uint_as_float(q) * __uint_as_float(k); }
   __device__ static void widen(uint32_t w, float* out) { out[0] = __uint_as_float(w); }
 };
 
@@ -49,6 +50,13 @@ struct ElemF16 {
   __device__ static float dot(uint32_t q, uint32_t k, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q), __builtin_bit_cast(f16x2, k),
                                   acc, false);
+  }
+  // First product of a chain, with the zero accumulator as an inline constant (the
+  // two-operand form the compiler prefers would need a register cleared first).
+  __device__ static float dot0(uint32_t q, uint32_t k) {
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(q), "v"(k));
+    return r;
   }
   __device__ static void widen(uint32_t w, float* out) {
     const f16x2 h = __builtin_bit_cast(f16x2, w);
@@ -63,381 +71,498 @@ struct ElemBF16 {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q),
                                            __builtin_bit_cast(bf16x2, k), acc, false);
   }
+  __device__ static float dot0(uint32_t q, uint32_t k) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(q), "v"(k));
+    return r;
+  }
   __device__ static void widen(uint32_t w, float* out) {
     out[0] = __uint_as_float(w << 16);
     out[1] = __uint_as_float(w & 0xffff0000u);
   }
 };
 
-// Orders this wave's LDS accesses around the call (LDS operations of one wave
-// execute in issue order, so only the compiler has to be held back).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Materializes x here: keeps the compiler from sinking the computation of x into
 // a branch when x feeds a lane-dependent select (which would split the scheduling
 // region of the surrounding loop).
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
-template <int kXor>
-__device__ __forceinline__ float dpp_xor_add(float x) {
-  // quad_perm patterns: [1,0,3,2] swaps neighbours, [2,3,0,1] swaps pairs.
-  constexpr int ctrl = kXor == 1 ? 0xB1 : 0x4E;
-  const int y = __builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false);
-  return x + __int_as_float(y);
-}
-
 // ------------------------------------------------------------------ decode partitions
 // One workgroup of kDecodeWaves waves per (sequence, KV head, partition of
 // partition_tokens tokens).  The waves take the partition's 16-token tiles in turn
 // (wave w: tiles w, w+4, ...); each tile of one KV head is a contiguous
-// 16 x 128-element run inside one physical block.
-//
-// Per tile and wave:
-//   * K and V rows arrive with 16-byte loads, a quarter-wave covering 256
-//     contiguous bytes; the next tile's loads are issued before this tile's math.
-//   * K goes to LDS with rows padded by 16 bytes, so lanes reading the same chunk of
-//     different rows hit different banks and every chunk is a constant offset from
-//     the lane's row address.
-//   * QK: lane (head hq, token t) takes whole-row dot products of its query head with
-//     K rows read back from LDS, so all G query heads of the group share one read of
-//     K from memory; for G < 4 a dot product is split over LPP lanes and summed with
-//     DPP.
+// 16 x 128-element run inside one physical block, read as kLoads 1 KiB wave-wide loads
+// (lane l takes the 16-byte chunk l of each KiB, so a token row is NCH consecutive
+// lanes).  K never passes through LDS:
+//   * QK: each lane dots its own 8 (fp32: 4) K elements with the same elements of all
+//     G query heads of the group, then a butterfly over the 16 lanes of its DPP row
+//     sums the partial dot products.  The first log2(G) steps are a reduce-scatter
+//     (each step keeps half the heads and adds the partner's other half), the rest
+//     an all-reduce; the lane's q registers hold the heads in the order that makes
+//     every step a single DPP add.  Lane a of a row ends with the full score of
+//     head (a >> (4 - log2 G)) for its token.
 //   * Online softmax in base 2 against a per-head reference maximum that is raised
 //     (and the accumulators rescaled) only when a score passes it by kRescaleSlack.
-//   * Probabilities go through LDS to the PV layout: lane (token group, 16-byte
-//     chunk) keeps o[G][chunk] for the tokens it loaded from V.
+//   * PV: the lane that loaded 16 bytes of a V row takes the G probabilities of that
+//     token from its own DPP row (row broadcasts) and accumulates o[G][chunk].
+//   * Each wave keeps the loads of its next tile or two in flight while it computes.
 // At the end the waves' (max, sum, o) are merged through LDS; a sequence with one
 // partition writes `out`, otherwise the partition writes its normalized o and its
 // base-2 log-sum-exp for the reduce kernel.
-template <class E, int G>
+template <class E, int GW>
 struct DecodeLds {
   static constexpr int NCH = kHeadDim * E::kBytes / 16;  // 16-byte chunks per K/V row
-  static constexpr int TG = kWave / NCH;                 // rows per wave-wide 16-byte load
-  struct Main {
-    u32x4 k[kDecodeWaves][kTileTokens][NCH + 1];  // +1: row padding against bank conflicts
-    float p[kDecodeWaves][kTileTokens][G];
-  };
-  struct Merge {
-    float o[kDecodeWaves][TG][G][kHeadDim];
-  };
-  union {
-    Main main;
-    Merge merge;
-  };
-  float m[kDecodeWaves][G];
-  float l[kDecodeWaves][G];
+  static constexpr int TG = kWave / NCH;                 // rows per wave-wide 1 KiB load
+  float o[kDecodeWaves][TG][GW][kHeadDim];
+  float m[kDecodeWaves][GW];
+  float l[kDecodeWaves][GW];
 };
 
-// One work item: (sequence, KV head, partition).  Every thread of the workgroup calls
-// this with the same item.
-template <class E, int G>
-__device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeLds<E, G>& lds, int seq,
-                                            int kvh, int part) {
-  constexpr int NCH = DecodeLds<E, G>::NCH;
-  constexpr int TG = DecodeLds<E, G>::TG;
-  constexpr int LOADS = kTileTokens / TG;         // 16-byte loads per lane per tile (K, and V)
-  constexpr int VD = 16 / E::kBytes;              // elements per 16-byte chunk
-  constexpr int LPP = G >= 4 ? 1 : 4 / G;         // lanes sharing one (head, token) dot product
-  constexpr int NPL = G >= 4 ? G / 4 : 1;         // (head, token) pairs per lane
-  constexpr int TSTRIDE = kWave / (LPP * G);      // token distance between a lane's pairs
-  constexpr int QCH = NCH / LPP;                  // 16-byte chunks of q per lane
+// DPP controls (16-lane rows): partner lane a ^ 8, a ^ 7, a ^ 2, a ^ 1 and broadcast of
+// lane k of the row.
+constexpr int kDppRor8 = 0x128;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppRowBcast0 = 0x150;
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int Hq = a.num_q_heads;
-  const int L = a.ctx[seq];
-  const bool bad_len = L < 0 || L > a.max_context ||
-                       static_cast<int64_t>(L) > static_cast<int64_t>(a.max_blocks) * a.block_size;
-  const size_t group_row = static_cast<size_t>(seq) * Hq + static_cast<size_t>(kvh) * G;
-  if (bad_len || L == 0) {
-    const float fill = bad_len ? __builtin_nanf("") : 0.0f;
-    for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x) a.out[group_row * kHeadDim + i] = fill;
-    return;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int G>
+struct GroupLayout {
+  static constexpr int kLog2 = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  static_assert((1 << kLog2) == G, "group size must be 1, 2, 4 or 8");
+  // Head whose full score lane position a (0..15) of a DPP row holds after the butterfly.
+  __device__ static int head_of_lane(int a) { return G == 1 ? 0 : (a >> (4 - kLog2)) & (G - 1); }
+  // First lane position of a row holding head h.
+  static constexpr int lane_of_head(int h) { return G == 1 ? 0 : h << (4 - kLog2); }
+  // Head held in q slot p by a lane whose final head is hs.
+  __device__ static int slot_head(int hs, int p) { return hs ^ (G == 8 ? (p ^ ((p >> 1) & 1)) : p); }
+};
+
+// s[i][0..G) holds the partial dot products of load i in slot order; on return
+// s[i][0] is the full 16-lane sum for head_of_lane(lane & 15).  The loads go through
+// each level together, so consecutive DPP instructions are independent.
+template <int G, int N>
+__device__ __forceinline__ void row_butterfly(float (&s)[N][G]) {
+  if constexpr (G >= 2) {
+#pragma unroll
+    for (int k = 0; k < G / 2; ++k)
+#pragma unroll
+      for (int i = 0; i < N; ++i) s[i][k] += dpp<kDppRor8>(s[i][G / 2 + k]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) s[i][0] += dpp<kDppRor8>(s[i][0]);
   }
-  const int t_begin = part * a.partition_tokens;
-  const int t_end = min(L, t_begin + a.partition_tokens);
-  const int n_tiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
-  const int n_parts = (L + a.partition_tokens - 1) / a.partition_tokens;
-
-  // QK role of this lane.
-  const int sub = lane % LPP;
-  const int hq = (lane / LPP) % G;
-  const int tq = (lane / LPP) / G;
-  // PV (and load) role of this lane.
-  const int tg = lane / NCH;
-  const int ch = lane % NCH;
-
-  u32x4 qv[QCH];
-  {
-    const u32x4* qsrc = reinterpret_cast<const u32x4*>(a.q) + (group_row + hq) * NCH + sub * QCH;
+  if constexpr (G >= 4) {
 #pragma unroll
-    for (int c = 0; c < QCH; ++c) qv[c] = qsrc[c];
+    for (int k = 0; k < G / 4; ++k)
+#pragma unroll
+      for (int i = 0; i < N; ++i) s[i][k] += dpp<kDppHalfMirror>(s[i][G / 4 + k]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) s[i][0] += dpp<kDppHalfMirror>(s[i][0]);
   }
-
-  float o[G][VD];
+  if constexpr (G >= 8) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int i = 0; i < N; ++i) s[i][0] += dpp<kDppXor2>(s[i][1]);
+  } else {
 #pragma unroll
-    for (int e = 0; e < VD; ++e) o[h][e] = 0.0f;
-  float m_mine = -INFINITY;  // reference maximum of head hq (same on all its lanes)
-  float l_acc = 0.0f;
-  bool bad_blk = false;
-
-  const int32_t* tbl = a.tables + static_cast<size_t>(seq) * a.max_blocks;
-  const char* kbase = static_cast<const char*>(a.k_cache);
-  const char* vbase = static_cast<const char*>(a.v_cache);
-  const int64_t row_bytes = kHeadDim * E::kBytes;
-  const int64_t run_bytes = static_cast<int64_t>(a.block_size) * row_bytes;
-
-  // Block ids of this wave's tiles (wave, wave + 4, ...), one per lane, loaded once
-  // per partition; each tile takes its id with readlane, so no memory wait stands
-  // between one tile's loads and the next.  Entries past the sequence's last block
-  // are not read.  (partition_tokens <= 4096 keeps a wave's tiles within 64 lanes.)
-  int tbl_lane = 0;
-  {
-    const int j = wave + kDecodeWaves * lane;
-    if (j < n_tiles) tbl_lane = tbl[(t_begin + j * kTileTokens) / a.block_size];
-  }
-  // Wait for it here, before any K/V load is in flight: otherwise the compiler
-  // cannot prove inside the tile loop that it has landed and drains every
-  // outstanding load on each tile.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
-  auto tile_offset = [&](int j) -> int64_t {
-    const int t0 = t_begin + j * kTileTokens;
-    const int off = t0 % a.block_size;
-    int phys = __builtin_amdgcn_readlane(tbl_lane, (j - wave) / kDecodeWaves);
-    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(a.num_blocks)) {
-      bad_blk = true;
-      phys = 0;
-    }
-    return (static_cast<int64_t>(phys) * a.num_kv_heads + kvh) * run_bytes + off * row_bytes;
-  };
-
-  auto load_rows = [&](const char* base, int64_t off, u32x4 (&r)[LOADS]) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(base + off) + lane;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) r[i] = src[i * kWave];
-  };
-
-  // Tile j's K and V rows are in kr / vr on entry; tile jn's are on their way into
-  // the same registers on exit: K as soon as tile j's K is in LDS, V as soon as tile
-  // j's PV has consumed it.  Past the last tile the loads repeat tile j (cache hits)
-  // so that the count of loads in flight, and with it every wait, is the same on
-  // each pass.
-  auto process = [&](int j, int jn, int64_t cur_off, u32x4 (&kr)[LOADS], u32x4 (&vr)[LOADS]) {
-    const int t0 = t_begin + j * kTileTokens;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int r = i * TG + tg;
-      lds.main.k[wave][r][ch] = kr[i];
-    }
-    const int64_t next_off = jn < n_tiles ? tile_offset(jn) : cur_off;
-    load_rows(kbase, next_off, kr);
-    wave_sync();
-
-    // QK, software-pipelined by hand: the K chunks of all NPL rows are read
-    // kAhead chunks before they are used; the scheduling fences keep the compiler
-    // from hoisting every read of the row at once (which would need 64 registers
-    // per row).
-    constexpr int kAhead = 2;
-    float acc[NPL][2];
-    u32x4 kk[kAhead + 1][NPL];
-#pragma unroll
-    for (int jj = 0; jj < NPL; ++jj) acc[jj][0] = acc[jj][1] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kAhead && c < QCH; ++c)
-#pragma unroll
-      for (int jj = 0; jj < NPL; ++jj) kk[c][jj] = lds.main.k[wave][tq + jj * TSTRIDE][sub * QCH + c];
-#pragma unroll
-    for (int c = 0; c < QCH; ++c) {
-      if (c + kAhead < QCH) {
-#pragma unroll
-        for (int jj = 0; jj < NPL; ++jj)
-          kk[(c + kAhead) % (kAhead + 1)][jj] =
-              lds.main.k[wave][tq + jj * TSTRIDE][sub * QCH + c + kAhead];
-      }
-#pragma unroll
-      for (int jj = 0; jj < NPL; ++jj) {
-        const u32x4 x = kk[c % (kAhead + 1)][jj];
-        acc[jj][0] = E::dot(qv[c].x, x.x, acc[jj][0]);
-        acc[jj][1] = E::dot(qv[c].y, x.y, acc[jj][1]);
-        acc[jj][0] = E::dot(qv[c].z, x.z, acc[jj][0]);
-        acc[jj][1] = E::dot(qv[c].w, x.w, acc[jj][1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    float z[NPL];
-#pragma unroll
-    for (int jj = 0; jj < NPL; ++jj) {
-      z[jj] = acc[jj][0] + acc[jj][1];
-      pin(z[jj]);
-    }
-    if constexpr (LPP >= 2) {
-#pragma unroll
-      for (int jj = 0; jj < NPL; ++jj) z[jj] = dpp_xor_add<1>(z[jj]);
-    }
-    if constexpr (LPP >= 4) {
-#pragma unroll
-      for (int jj = 0; jj < NPL; ++jj) z[jj] = dpp_xor_add<2>(z[jj]);
-    }
-    bool over = false;
-#pragma unroll
-    for (int jj = 0; jj < NPL; ++jj) {
-      const int t = tq + jj * TSTRIDE;
-      z[jj] = (t0 + t < t_end) ? z[jj] * a.scale_log2 : -INFINITY;
-      over |= z[jj] > m_mine + kRescaleSlack;
-    }
-
-    if (__builtin_amdgcn_ballot_w64(over) != 0) {
-      // Raise each head's reference maximum to the tile's maximum and rescale: the
-      // lanes of one head (same hq) reduce their scores, then every lane fetches the
-      // G rescale factors from the first lane of each head.
-      float tmax = z[0];
-#pragma unroll
-      for (int jj = 1; jj < NPL; ++jj) tmax = fmaxf(tmax, z[jj]);
-#pragma unroll
-      for (int m = LPP * G; m < kWave; m <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, m));
-      const float m_new = fmaxf(m_mine, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_mine - m_new);
-      l_acc *= alpha;
-      m_mine = m_new;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h * LPP));
-#pragma unroll
-        for (int e = 0; e < VD; ++e) o[h][e] *= ah;
-      }
-    }
-
-#pragma unroll
-    for (int jj = 0; jj < NPL; ++jj) {
-      const float pr = __builtin_amdgcn_exp2f(z[jj] - m_mine);
-      l_acc += pr;
-      if (sub == 0) lds.main.p[wave][tq + jj * TSTRIDE][hq] = pr;
-    }
-    wave_sync();
-
-    const bool partial_tile = t0 + kTileTokens > t_end;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int r = i * TG + tg;
-      float pv[G];
-      if constexpr (G % 4 == 0) {
-#pragma unroll
-        for (int h4 = 0; h4 < G / 4; ++h4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&lds.main.p[wave][r][h4 * 4]);
-          pv[h4 * 4 + 0] = x.x;
-          pv[h4 * 4 + 1] = x.y;
-          pv[h4 * 4 + 2] = x.z;
-          pv[h4 * 4 + 3] = x.w;
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < G; ++h) pv[h] = lds.main.p[wave][r][h];
-      }
-      float v[VD];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) E::widen(vr[i][w], &v[w * (VD / 4)]);
-      if (partial_tile) {
-        // Rows past the context may hold anything (even NaN): drop them by select.
-        const bool keep = t0 + r < t_end;
-#pragma unroll
-        for (int e = 0; e < VD; ++e) {
-          pin(v[e]);
-          v[e] = keep ? v[e] : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < VD; ++e) o[h][e] = fmaf(pv[h], v[e], o[h][e]);
-    }
-    load_rows(vbase, next_off, vr);
-    wave_sync();
-    return next_off;
-  };
-
-  {
-    u32x4 kr[LOADS], vr[LOADS];
-    if (wave < n_tiles) {
-      int64_t off = tile_offset(wave);
-      load_rows(kbase, off, kr);
-      load_rows(vbase, off, vr);
-      for (int j = wave; j < n_tiles; j += kDecodeWaves) off = process(j, j + kDecodeWaves, off, kr, vr);
-    }
-  }
-
-  // ---- merge the waves
-  if (bad_blk) l_acc = __builtin_nanf("");
-#pragma unroll
-  for (int m = LPP * G; m < kWave; m <<= 1) l_acc += __shfl_xor(l_acc, m);
-  __syncthreads();  // every wave is done with lds.main before lds.merge overwrites it
-  if (tq == 0 && sub == 0) {
-    lds.l[wave][hq] = l_acc;
-    lds.m[wave][hq] = m_mine;
+    for (int i = 0; i < N; ++i) s[i][0] += dpp<kDppXor2>(s[i][0]);
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e4 = 0; e4 < VD; e4 += 4)
-      *reinterpret_cast<f32x4*>(&lds.merge.o[wave][tg][h][ch * VD + e4]) =
-          f32x4{o[h][e4], o[h][e4 + 1], o[h][e4 + 2], o[h][e4 + 3]};
-  __syncthreads();
+  for (int i = 0; i < N; ++i) s[i][0] += dpp<kDppXor1>(s[i][0]);
+}
 
-  for (int idx = threadIdx.x; idx < G * (kHeadDim / 4); idx += blockDim.x) {
-    const int h = idx / (kHeadDim / 4);
-    const int d4 = (idx % (kHeadDim / 4)) * 4;
-    float M = -INFINITY;
+// Lane h of each 16-lane row, broadcast to the row (every lane is written, so no old
+// value is needed).
+template <int H>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_mov_dpp(__float_as_int(x), kDppRowBcast0 + H, 0xF, 0xF, true));
+}
+
+// acc += (p of lane LANE of this 16-lane row) * v, as one DPP FMA.  Volatile keeps the
+// FMAs after the s_nop that precedes them (the compiler cannot see the DPP read).
+template <int LANE>
+__device__ __forceinline__ void fma_row_bcast(float& acc, float p, float v) {
+  asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+               : "+v"(acc)
+               : "v"(p), "v"(v), "i"(LANE));
+}
+
+template <int GW, int VD, int H>
+__device__ __forceinline__ void pv_row(float (&o)[GW][VD], float pr, const float (&v)[VD]) {
+  if constexpr (H < GW) {
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, lds.m[w][h]);
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    float lt = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float W = __builtin_amdgcn_exp2f(lds.m[w][h] - M);
-      lt += W * lds.l[w][h];
-      f32x4 sum = *reinterpret_cast<const f32x4*>(&lds.merge.o[w][0][h][d4]);
-#pragma unroll
-      for (int g = 1; g < TG; ++g) sum += *reinterpret_cast<const f32x4*>(&lds.merge.o[w][g][h][d4]);
-      acc += W * sum;
-    }
-    const f32x4 res = acc / lt;
-    const size_t row = group_row + h;
-    if (n_parts == 1) {
-      *reinterpret_cast<f32x4*>(a.out + row * kHeadDim + d4) = res;
-    } else {
-      const size_t prow = row * a.pmax + part;
-      *reinterpret_cast<f32x4*>(a.part_o + prow * kHeadDim + d4) = res;
-      if (d4 == 0) a.part_lse[prow] = M + __log2f(lt);
-    }
+    for (int e = 0; e < VD; ++e) fma_row_bcast<GroupLayout<GW>::lane_of_head(H)>(o[H][e], pr, v[e]);
+    pv_row<GW, VD, H + 1>(o, pr, v);
   }
 }
 
-// Persistent decode workgroups: each takes (item, KV head) work numbers from the
-// counter the plan kernel zeroed, until the numbers run out; the next number is
-// fetched while the current item runs.
-template <class E, int G>
-__global__ __launch_bounds__(kWave * kDecodeWaves, 2) void decode_partition_kernel(const DecodeArgs a) {
-  __shared__ DecodeLds<E, G> lds;
-  __shared__ int s_next;
-  int* counter = a.work_header;
-  const int n_work = a.work_header[1];
-  if (threadIdx.x == 0) s_next = atomicAdd(counter, 1);
-  __syncthreads();
-  int work = s_next;
-  while (work < n_work) {
-    __syncthreads();  // s_next has been read and the previous item's LDS is free
-    if (threadIdx.x == 0) s_next = atomicAdd(counter, 1);
+// Loads through the scalar data cache: for data that no kernel writes while this one
+// runs (the work list), at a wave-uniform address.
+template <class T>
+__device__ __forceinline__ T ld_uniform(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)(p))[i];
+}
+
+// One work unit: (sequence, KV head, partition) and the sequence's context length,
+// wave-uniform.  Everything else is derived from these four numbers when needed.
+struct Unit {
+  int seq, kvh, part, L;
+};
+
+// Persistent decode workgroups.  Each claims work numbers (item, KV head) from the
+// counter the plan kernel zeroed, one ahead of the one it runs, until they run out.
+// While a unit runs, the next one is made ready: its descriptor (scalar loads), the
+// row offsets of its tiles, its query rows (staged through LDS) and its first two K/V
+// tiles (issued by the last iterations of the current tile loop), so consecutive units
+// run back to back.
+// Workgroups per CU the register budget is sized for: the more query heads a wave
+// carries (query and output registers), the fewer workgroups fit.
+template <class E, int GW>
+constexpr int decode_blocks_per_cu() {
+  return E::kBytes == 4 ? 2 : (GW >= 8 ? 2 : GW >= 4 ? 3 : 4);
+}
+
+template <class E, int GW, int HS>
+__global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>())) void decode_partition_kernel(const DecodeArgs a) {
+  constexpr int G = GW * HS;            // query heads per KV head
+  constexpr int NS = kDecodeWaves / HS;  // tile streams per workgroup
+  using GL = GroupLayout<GW>;
+  using Lds = DecodeLds<E, GW>;
+  constexpr int NCH = Lds::NCH;
+  constexpr int TG = Lds::TG;
+  constexpr int LOADS = kTileTokens / TG;  // 1 KiB loads per tile (K, and again V)
+  constexpr int VD = 16 / E::kBytes;       // elements per 16-byte chunk
+  constexpr int QDW = G * kHeadDim * E::kBytes / 4;  // dwords of one group's query rows
+  constexpr int QPT = (QDW + kWave * kDecodeWaves - 1) / (kWave * kDecodeWaves);
+  constexpr int64_t kRowBytes = kHeadDim * E::kBytes;
+
+  __shared__ Lds lds;
+  __shared__ u32x4 s_q[G * NCH];  // query rows of the next unit
+  __shared__ int s_claim[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int stream = wave % NS;  // takes the unit's tiles stream, stream + NS, ...
+  const int half = wave / NS;    // takes query heads half * GW .. half * GW + GW - 1
+  const int rr = lane / NCH;  // token row of the lane within each 1 KiB load
+  const int ch = lane % NCH;  // 16-byte chunk of that row
+  const int hsel = GL::head_of_lane(lane & 15);
+  const int P = a.partition_tokens;
+
+  auto unit_of = [&](int work) -> Unit {
+    Unit u;
     const int item = work / a.num_kv_heads;
-    decode_item<E, G>(a, lds, a.work_items[2 * item], work - item * a.num_kv_heads,
-                      a.work_items[2 * item + 1]);
-    __syncthreads();
-    work = s_next;
+    u.kvh = work - item * a.num_kv_heads;
+    u.seq = ld_uniform(a.work_items, 4 * static_cast<int64_t>(item));
+    u.part = ld_uniform(a.work_items, 4 * static_cast<int64_t>(item) + 1);
+    u.L = ld_uniform(a.work_items, 4 * static_cast<int64_t>(item) + 2);
+    return u;
+  };
+  // Empty (zeros) or invalid (NaNs) sequences have no tiles.
+  auto is_bad = [&](const Unit& u) {
+    return u.L < 0 || u.L > a.max_context ||
+           static_cast<int64_t>(u.L) > static_cast<int64_t>(a.max_blocks) * a.block_size;
+  };
+  auto t_end_of = [&](const Unit& u) {
+    return (is_bad(u) || u.L == 0) ? u.part * P : min(u.L, u.part * P + P);
+  };
+  // Number of tiles this wave takes in a unit (tiles stream, stream + NS, ...).
+  auto wave_tiles = [&](const Unit& u) {
+    const int n_tiles = (t_end_of(u) - u.part * P + kTileTokens - 1) / kTileTokens;
+    return stream < n_tiles ? (n_tiles - stream + NS - 1) / NS : 0;
+  };
+  // Row offset (rows of head_dim elements from the layer's K base) of the wave's tile
+  // `lane`, or -1 if its block id lies outside the pool; 0 for lanes past the wave's
+  // tiles.  partition_tokens <= kMaxPartition keeps a wave's tiles within 64 lanes.
+  auto tile_rows = [&](const Unit& u, int nt) -> int {
+    if (lane >= nt) return 0;
+    const int t0 = u.part * P + (stream + NS * lane) * kTileTokens;
+    const int phys = a.tables[static_cast<int64_t>(u.seq) * a.max_blocks + t0 / a.block_size];
+    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(a.num_blocks)) return -1;
+    return (phys * a.num_kv_heads + u.kvh) * a.block_size + t0 % a.block_size;
+  };
+  auto load_q = [&](const Unit& u, uint32_t (&qd)[QPT]) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.q) +
+                          (static_cast<int64_t>(u.seq) * a.num_q_heads + u.kvh * G) * (QDW / G);
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int d = tid + i * kWave * kDecodeWaves;
+      qd[i] = d < QDW ? src[d] : 0u;
+    }
+  };
+  auto stage_q = [&](const uint32_t (&qd)[QPT]) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(s_q);
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int d = tid + i * kWave * kDecodeWaves;
+      if (d < QDW) dst[d] = qd[i];
+    }
+  };
+
+  if (tid == 0) {
+    s_claim[0] = atomicAdd(a.work_header, 1);
+    s_claim[1] = atomicAdd(a.work_header, 1);
+  }
+  __syncthreads();
+  const int n_work = ld_uniform(a.work_header, 1);
+  int cur = __builtin_amdgcn_readfirstlane(s_claim[0]);
+  int nxt = __builtin_amdgcn_readfirstlane(s_claim[1]);
+  if (cur >= n_work) return;
+
+  Unit it = unit_of(cur);
+  int nt = wave_tiles(it);
+  int rows_cur = tile_rows(it, nt);
+  {
+    uint32_t qd[QPT];
+    load_q(it, qd);
+    stage_q(qd);
+  }
+  bool prefetched = false;  // kr / vr already hold (or are receiving) the unit's tile 0
+  u32x4 kr[LOADS], vr[LOADS];
+  const char* kbase = static_cast<const char*>(a.k_cache);
+  const char* vbase = static_cast<const char*>(a.v_cache);
+
+  while (true) {
+    __syncthreads();  // s_q is staged; s_claim and the previous unit's LDS are free
+    // The claim's result is needed only at the end of the unit: it stays in a register
+    // until then, so that nothing waits for the atomic here.
+    int claimed = 0;
+    if (tid == 0) claimed = atomicAdd(a.work_header, 1);
+    const bool has_next = nxt < n_work;
+    const Unit nx = unit_of(has_next ? nxt : cur);
+    const int nt_nx = has_next ? wave_tiles(nx) : 0;
+    const int t_begin = it.part * P;
+    const int t_end = t_end_of(it);
+
+    u32x4 qv[GW];
+    {
+      // Recomputed per unit on purpose: hoisted out of the loop, the G addresses would
+      // stay live through the tile loop and spill.
+      int hs = hsel;
+      asm volatile("" : "+v"(hs));
+#pragma unroll
+      for (int p = 0; p < GW; ++p) qv[p] = s_q[(half * GW + GL::slot_head(hs, p)) * NCH + ch];
+    }
+
+    // Tile n of the wave's stream: this unit's tiles, then (when the next unit has
+    // tiles on this wave) the next unit's first one; else this unit's last tile again
+    // (a cache hit), so every pass has the same loads in flight and the same waits.
+    const bool cross = nt_nx > 0;
+    int rows_next = 0;
+    // A block id outside the pool (row offset -1) makes the unit's result NaN; such
+    // tiles are read from block 0 instead, so nothing outside the pool is touched.
+    const bool bad_blk = __builtin_amdgcn_ballot_w64(lane < nt && rows_cur < 0) != 0;
+    auto issue = [&](int n, const char* base, u32x4 (&r)[LOADS]) {
+      int rows = (n >= nt && cross) ? __builtin_amdgcn_readlane(rows_next, 0)
+                                    : __builtin_amdgcn_readlane(rows_cur, min(n, nt - 1));
+      rows = max(rows, 0);
+      const u32x4* src = reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(rows) * kRowBytes) + lane;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) r[i] = src[i * kWave];
+    };
+
+    // The next unit's row offsets and query rows, loaded once this unit is under way.
+    uint32_t qn[QPT];
+    bool next_loaded = false;
+    auto load_next = [&]() {
+      rows_next = has_next ? tile_rows(nx, nt_nx) : 0;
+      if (has_next) load_q(nx, qn);
+      next_loaded = true;
+    };
+
+    if (nt > 0 && !prefetched) {
+      issue(0, kbase, kr);
+      issue(0, vbase, vr);
+    }
+
+    float o[GW][VD];
+#pragma unroll
+    for (int h = 0; h < GW; ++h)
+#pragma unroll
+      for (int e = 0; e < VD; ++e) o[h][e] = 0.0f;
+    float m_ref = -INFINITY;  // reference maximum of head hsel (same on all its lanes)
+    float l_acc = 0.0f;       // sum of this lane's probabilities (head hsel, its rows)
+
+    // Tile n's K and V are in kr / vr on entry; tile n + 1's are on their way into the
+    // same registers on exit, each issued as soon as tile n has consumed the registers.
+    auto process = [&](int n) {
+      const int t0 = t_begin + (stream + NS * n) * kTileTokens;
+      // Partial dot products of every load first, then the butterflies of all loads
+      // level by level, so that no DPP step waits on the instruction just before it.
+      float s[LOADS][GW];
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+#pragma unroll
+        for (int p = 0; p < GW; ++p) {
+          float acc = E::dot0(qv[p].x, kr[i].x);
+          acc = E::dot(qv[p].y, kr[i].y, acc);
+          acc = E::dot(qv[p].z, kr[i].z, acc);
+          s[i][p] = E::dot(qv[p].w, kr[i].w, acc);
+        }
+      if (n == 0) load_next();
+      issue(n + 1, kbase, kr);
+      if constexpr (NCH == 32) {
+        // A row spans two DPP rows: add the other half of the row first.
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+#pragma unroll
+          for (int p = 0; p < GW; ++p) s[i][p] += __shfl_xor(s[i][p], 16);
+      }
+      row_butterfly<GW, LOADS>(s);
+      float z[LOADS];
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        pin(s[i][0]);
+        const int t = t0 + i * TG + rr;
+        z[i] = t < t_end ? s[i][0] * a.scale_log2 : -INFINITY;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      bool over = false;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) over |= z[i] > m_ref + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+        // Raise each head's reference maximum to the tile's maximum and rescale.  Lanes
+        // of one head within a row hold the same scores; rows of other tokens are other
+        // lanes 16 (or 32) apart.
+        float tmax = z[0];
+#pragma unroll
+        for (int i = 1; i < LOADS; ++i) tmax = fmaxf(tmax, z[i]);
+#pragma unroll
+        for (int m = NCH; m < kWave; m <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, m));
+        const float m_new = fmaxf(m_ref, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+        l_acc *= alpha;
+        m_ref = m_new;
+#pragma unroll
+        for (int h = 0; h < GW; ++h) {
+          const float ah =
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), GL::lane_of_head(h)));
+#pragma unroll
+          for (int e = 0; e < VD; ++e) o[h][e] *= ah;
+        }
+      }
+
+      const bool partial_tile = t0 + kTileTokens > t_end;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const float pr = __builtin_amdgcn_exp2f(z[i] - m_ref);
+        l_acc += pr;
+        float v[VD];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) E::widen(vr[i][w], &v[w * (VD / 4)]);
+        if (partial_tile) {
+          // Rows past the context may hold anything (even NaN): drop them by select.
+          const bool keep = t0 + i * TG + rr < t_end;
+#pragma unroll
+          for (int e = 0; e < VD; ++e) {
+            pin(v[e]);
+            v[e] = keep ? v[e] : 0.0f;
+          }
+        }
+        if constexpr (GW == 1) {
+#pragma unroll
+          for (int e = 0; e < VD; ++e) o[0][e] = fmaf(pr, v[e], o[0][e]);
+        } else {
+          // o[h] += p(head h, this row) * v: the probability comes straight from the
+          // lane holding head h through the FMA's row broadcast.  Two wait states
+          // separate the write of pr from its first DPP read.
+          // (pr is an operand of the s_nop so that its computation cannot be scheduled
+          // between the s_nop and the FMAs.)
+          asm volatile("s_nop 1" ::"v"(pr));
+          pv_row<GW, VD, 0>(o, pr, v);
+        }
+        // One load's probabilities and V values at a time: interleaving the loads
+        // would keep all of them live and spill.
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      issue(n + 1, vbase, vr);
+    };
+
+    for (int n = 0; n < nt; ++n) process(n);
+    if (!next_loaded) load_next();
+    prefetched = nt > 0 && cross;
+
+    // ---- merge the waves and write the unit's result
+    const size_t group_row = static_cast<size_t>(it.seq) * a.num_q_heads + static_cast<size_t>(it.kvh) * G;
+    if (t_end == t_begin) {
+      // Empty sequence (zeros) or invalid one (NaNs); a unit with tiles is never empty.
+      const float fill = is_bad(it) ? __builtin_nanf("") : 0.0f;
+      for (int i = tid; i < G * kHeadDim; i += blockDim.x) a.out[group_row * kHeadDim + i] = fill;
+      __syncthreads();  // every wave has read s_q before it is restaged
+    } else {
+      if (bad_blk) l_acc = __builtin_nanf("");
+#pragma unroll
+      for (int h = 0; h < GW; ++h) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < TG; ++r)
+          sum += __int_as_float(
+              __builtin_amdgcn_readlane(__float_as_int(l_acc), r * NCH + GL::lane_of_head(h)));
+        const float mh =
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_ref), GL::lane_of_head(h)));
+        if (lane == 0) {
+          lds.m[wave][h] = mh;
+          lds.l[wave][h] = sum;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GW; ++h)
+#pragma unroll
+        for (int e4 = 0; e4 < VD; e4 += 4)
+          *reinterpret_cast<f32x4*>(&lds.o[wave][rr][h][ch * VD + e4]) =
+              f32x4{o[h][e4], o[h][e4 + 1], o[h][e4 + 2], o[h][e4 + 3]};
+      __syncthreads();
+
+      const int n_parts = (it.L + P - 1) / P;
+      for (int idx = tid; idx < G * (kHeadDim / 4); idx += blockDim.x) {
+        const int h = idx / (kHeadDim / 4);
+        const int d4 = (idx % (kHeadDim / 4)) * 4;
+        const int hw = h % GW;        // head within its wave
+        const int w0 = (h / GW) * NS;  // first wave holding head h (one per stream)
+        float M = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) M = fmaxf(M, lds.m[w0 + j][hw]);
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        float lt = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const int w = w0 + j;
+          const float W = __builtin_amdgcn_exp2f(lds.m[w][hw] - M);
+          lt += W * lds.l[w][hw];
+          f32x4 sum = *reinterpret_cast<const f32x4*>(&lds.o[w][0][hw][d4]);
+#pragma unroll
+          for (int r = 1; r < TG; ++r) sum += *reinterpret_cast<const f32x4*>(&lds.o[w][r][hw][d4]);
+          acc += W * sum;
+        }
+        const f32x4 res = acc / lt;
+        const size_t row = group_row + h;
+        if (n_parts == 1) {
+          *reinterpret_cast<f32x4*>(a.out + row * kHeadDim + d4) = res;
+        } else {
+          const size_t prow = row * a.pmax + it.part;
+          *reinterpret_cast<f32x4*>(a.part_o + prow * kHeadDim + d4) = res;
+          if (d4 == 0) a.part_lse[prow] = M + __log2f(lt);
+        }
+      }
+    }
+    if (!has_next) break;
+    stage_q(qn);  // s_q was last read at this unit's start, before a barrier
+    if (tid == 0) s_claim[0] = claimed;
+    __syncthreads();  // s_claim[0] is visible; the merge is done with lds
+    cur = nxt;
+    nxt = __builtin_amdgcn_readfirstlane(s_claim[0]);
+    it = nx;
+    nt = nt_nx;
+    rows_cur = rows_next;
   }
 }
 
@@ -502,13 +627,20 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeA
     int tf, tp;
     const int fo = block_exclusive_scan(f, s_tmp, &tf) + full_base;
     const int po = block_exclusive_scan(pp, s_tmp, &tp) + part_base;
+    const int L = s < a.num_seqs ? a.ctx[s] : 0;
     for (int k = 0; k < f; ++k) {
-      a.work_items[2 * (fo + k)] = s;
-      a.work_items[2 * (fo + k) + 1] = k;
+      int32_t* d = a.work_items + 4 * (fo + k);
+      d[0] = s;
+      d[1] = k;
+      d[2] = L;
+      d[3] = 0;
     }
     if (pp) {
-      a.work_items[2 * po] = s;
-      a.work_items[2 * po + 1] = f;
+      int32_t* d = a.work_items + 4 * po;
+      d[0] = s;
+      d[1] = f;
+      d[2] = L;
+      d[3] = 0;
     }
     full_base += tf;
     part_base += tp;
@@ -606,7 +738,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* __restr
   for (; c < block_chunks; c += 256) d[c] = s[c];
 }
 
-template <class E, int G>
+template <class E, int GW, int HS>
 hipError_t launch_persistent(const DecodeArgs& a, hipStream_t s) {
   // Workgroups resident at once on the current device (cached per device).
   static int cached[64] = {0};
@@ -616,7 +748,7 @@ hipError_t launch_persistent(const DecodeArgs& a, hipStream_t s) {
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (cached[dev] == 0) {
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partition_kernel<E, G>,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partition_kernel<E, GW, HS>,
                                                      kWave * kDecodeWaves, 0);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -625,7 +757,7 @@ hipError_t launch_persistent(const DecodeArgs& a, hipStream_t s) {
   }
   const int64_t upper = static_cast<int64_t>(a.num_seqs) * a.pmax * a.num_kv_heads;
   const int grid = static_cast<int>(std::min<int64_t>(cached[dev], upper));
-  hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_partition_kernel<E, G>), dim3(grid),
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_partition_kernel<E, GW, HS>), dim3(grid),
                      dim3(kWave * kDecodeWaves), 0, s, a);
   return hipGetLastError();
 }
@@ -633,10 +765,13 @@ hipError_t launch_persistent(const DecodeArgs& a, hipStream_t s) {
 template <class E>
 hipError_t launch_decode_typed(const DecodeArgs& a, int group, hipStream_t s) {
   switch (group) {
-    case 1: return launch_persistent<E, 1>(a, s);
-    case 2: return launch_persistent<E, 2>(a, s);
-    case 4: return launch_persistent<E, 4>(a, s);
-    case 8: return launch_persistent<E, 8>(a, s);
+    // One wave carries the whole group (HS = 1).  HS = 2 would split a group over two
+    // waves that read the same K/V tiles; measured slower for groups of 8 (the
+    // duplicated loads and conversions outweigh the register savings).
+    case 1: return launch_persistent<E, 1, 1>(a, s);
+    case 2: return launch_persistent<E, 2, 1>(a, s);
+    case 4: return launch_persistent<E, 4, 1>(a, s);
+    case 8: return launch_persistent<E, 8, 1>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -14,7 +14,9 @@ constexpr int kTileTokens = 16;      // tokens per K/V tile streamed by the deco
 constexpr int kDecodeWaves = 4;      // waves per decode workgroup
 constexpr int kDefaultPartition = 512;
 constexpr int kPlanThreads = 1024;
-constexpr int kMaxPartition = kDecodeWaves * 64 * kTileTokens;  // a wave's tiles fit one wave of lanes
+// A wave's tiles of one unit must fit one wave of lanes; a workgroup has at least two
+// tile streams (four waves, at most two head halves).
+constexpr int kMaxPartition = 2 * 64 * kTileTokens;
 
 struct DecodeArgs {
   const void* q;            // [S][Hq][128]
@@ -26,7 +28,7 @@ struct DecodeArgs {
   float* part_o;            // [S][Hq][pmax][128]
   float* part_lse;          // [S][Hq][pmax], base-2 log-sum-exp of scaled scores
   int32_t* work_header;     // [0] work counter, [1] number of (item, KV head) work units
-  int32_t* work_items;      // [S * pmax][2] (sequence, partition)
+  int32_t* work_items;      // [S * pmax][4] (sequence, partition, context length, 0)
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks, num_blocks, block_size;
   int32_t max_context, partition_tokens, pmax;
   float scale_log2;         // scale * log2(e)

@@ -119,13 +119,16 @@ def llama2_7b(seed=2, num_seqs=64, min_len=128, max_len=2048):
     return _decode_workload("llama2_7b", rng, F16, lens, 32, 32, 128, 16, N)
 
 
-def llama3_70b(seed=3, num_seqs=128, min_len=256, max_len=8192):
-    """Llama-3-70B-shaped GQA layer: 64 query / 8 KV heads, bf16, log-uniform lengths."""
+def llama3_70b(seed=3, num_seqs=128, min_len=256, max_len=8192, num_q_heads=64, fixed_len=0):
+    """Llama-3-70B-shaped GQA layer: 64 query / 8 KV heads, bf16, log-uniform lengths
+    (or every sequence ``fixed_len`` tokens long when that is given)."""
     rng = np.random.default_rng(seed)
     u = rng.random(num_seqs)
     lens = np.clip(np.floor(min_len * (max_len / min_len) ** u), min_len, max_len).astype(np.int64)
+    if fixed_len:
+        lens = np.full(num_seqs, fixed_len, dtype=np.int64)
     N = math.ceil(1.25 * sum(_blocks(L, 16) for L in lens))
-    return _decode_workload("llama3_70b", rng, BF16, lens, 64, 8, 128, 16, N)
+    return _decode_workload("llama3_70b", rng, BF16, lens, num_q_heads, 8, 128, 16, N)
 
 
 def custom_decode(seed, dtype, lens, num_q_heads, num_kv_heads, head_dim=128, block_size=16,
