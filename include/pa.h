@@ -215,6 +215,38 @@ int pa_decode_reduce(pa_pool* pool, int32_t layer, const void* q, int32_t num_se
                      int32_t partition_tokens, float* out, void* workspace,
                      int64_t workspace_bytes, void* stream);
 
+/* Chunked prefill of one layer: causal attention of the query rows of several
+ *   sequences, each over that sequence's paged cache ("LLM inference optimization: KV
+ *   cache & PagedAttention", carlstack.gravito.dev, section 六 item 2: long prompts in
+ *   chunks, batched with decode work; "vLLM explained", appendix).  Sequence s owns query
+ *   rows query_start[s] .. query_start[s+1] - 1; with n_s rows and context length L_s,
+ *   its row i is the token at position L_s - n_s + i (so its K/V, like the whole chunk's,
+ *   must already be in the cache: write them with pa_reshape_and_cache first) and
+ *       out[row][h] = softmax(scale * q[row][h] . K^T) V  over tokens 0 .. L_s - n_s + i
+ *   of the sequence, KV head h / (num_q_heads / num_kv_heads).  A decode row is the case
+ *   n_s = 1.  QK^T and PV run on the matrix cores (fp16 / bf16 inputs, fp32 accumulation;
+ *   the probabilities enter as a 16-bit value plus the 16-bit rounding of the rest).
+ *
+ *   q            device [num_rows][num_q_heads][head_dim], pool dtype, contiguous
+ *   query_start  device int32 [num_seqs + 1], nondecreasing, query_start[num_seqs] <= num_rows
+ *   block_tables device int32 [num_seqs][max_blocks]; entries past a sequence's last
+ *                block are never read
+ *   context_lens device int32 [num_seqs]
+ *   max_context  host bound on context_lens
+ *   max_query_len host bound on every n_s (sizes the grid: rows past it are not computed)
+ *   out          device fp32 [num_rows][num_q_heads][head_dim]
+ * A sequence with n_s > L_s, L_s > max_context or L_s > max_blocks * block_size, or whose
+ * keys touch a table id outside [0, num_blocks), gets NaN rows; nothing outside the pool
+ * or the row range is read or written.  Rows not owned by any sequence are untouched.
+ * No workspace is needed.  Supported: head_dim 128; fp16 and bf16 caches
+ * (PA_E_UNSUPPORTED for fp32); num_q_heads / num_kv_heads in {1, 2, 4, 8}; block_size a
+ * multiple of 16; at most 65535 sequences per call. */
+int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_rows,
+                       int32_t num_q_heads, const int32_t* query_start, int32_t num_seqs,
+                       const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                       int32_t max_context, int32_t max_query_len, float scale, float* out,
+                       void* stream);
+
 /* Thread-local message of the last failed call on this thread ("" if none). */
 const char* pa_last_error(void);
 

@@ -64,6 +64,8 @@ _SIGNATURES = {
     "pa_decode_plan": (ctypes.c_int, _DECODE_ARGS),
     "pa_decode_partitions": (ctypes.c_int, _DECODE_ARGS),
     "pa_decode_reduce": (ctypes.c_int, _DECODE_ARGS),
+    "pa_prefill_chunked": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _I32,
+                                          _I32, ctypes.c_float, _P, _P]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 
@@ -304,3 +306,19 @@ def pa_decode_reduce(pool, layer, q, block_tables, context_lens, max_context, sc
                      workspace, partition_tokens=0, stream=None):
     _decode(lib().pa_decode_reduce, pool, layer, q, block_tables, context_lens, max_context,
             scale, out, workspace, partition_tokens, stream)
+
+
+def pa_prefill_chunked(pool, layer, q, query_start, block_tables, context_lens, max_context,
+                       max_query_len, scale, out, stream=None):
+    """q: GPU ``[R][H_q][d]`` pool dtype; query_start: GPU int32 ``[S+1]``; out: GPU fp32
+    ``[R][H_q][d]``."""
+    import torch
+    R, H_q = q.shape[0], q.shape[1]
+    S = query_start.numel() - 1
+    _check(lib().pa_prefill_chunked(pool.handle, layer, _dev(q, torch_dtype(pool.desc.kv_dtype), "q"),
+                                    R, H_q, _dev(query_start, torch.int32, "query_start"), S,
+                                    _dev(block_tables, torch.int32, "block_tables"),
+                                    block_tables.shape[1],
+                                    _dev(context_lens, torch.int32, "context_lens"), max_context,
+                                    max_query_len, float(scale), _dev(out, torch.float32, "out"),
+                                    _stream(stream)))

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libpa.so")
 
-SOURCES = ["capi.cpp", "block_manager.cpp", "kernels.hip"]
+SOURCES = ["capi.cpp", "block_manager.cpp", "kernels.hip", "prefill.hip"]
 
 # Packed-FP32 VALU forms are kept out of the generated code on purpose; the host
 # pass warns that it does not know the feature, which is harmless.

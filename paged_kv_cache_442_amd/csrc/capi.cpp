@@ -15,6 +15,7 @@
 
 #include "block_manager.hpp"
 #include "kernels.hpp"
+#include "prefill.hpp"
 
 struct pa_pool {
   pa_pool_desc desc;
@@ -455,6 +456,64 @@ int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs, int
   return pa_decode_reduce(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
                           context_lens, max_context, scale, partition_tokens, out, workspace,
                           workspace_bytes, stream);
+}
+
+int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_rows,
+                       int32_t num_q_heads, const int32_t* query_start, int32_t num_seqs,
+                       const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                       int32_t max_context, int32_t max_query_len, float scale, float* out,
+                       void* stream) {
+  int st = check_device_pool(pool, layer);
+  if (st) return st;
+  const pa_pool_desc& d = pool->desc;
+  if (num_rows < 0 || num_seqs < 0 || num_q_heads < 1 || max_blocks < 0 || max_context < 0 ||
+      max_query_len < 0)
+    return fail(PA_E_INVAL, "negative size (num_rows %d num_seqs %d num_q_heads %d max_blocks %d "
+                "max_context %d max_query_len %d)", num_rows, num_seqs, num_q_heads, max_blocks,
+                max_context, max_query_len);
+  if (num_q_heads % d.num_kv_heads != 0)
+    return fail(PA_E_INVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                d.num_kv_heads);
+  const int group = num_q_heads / d.num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PA_E_UNSUPPORTED, "query group size %d (supported: 1, 2, 4, 8)", group);
+  if (d.head_dim != pa::kHeadDim)
+    return fail(PA_E_UNSUPPORTED, "head_dim %d (supported: %d)", d.head_dim, pa::kHeadDim);
+  if (d.kv_dtype != PA_F16 && d.kv_dtype != PA_BF16)
+    return fail(PA_E_UNSUPPORTED, "chunked prefill runs on the matrix cores: fp16 or bf16 caches only");
+  if (d.block_size % 16 != 0)
+    return fail(PA_E_UNSUPPORTED, "block_size %d (must be a multiple of 16)", d.block_size);
+  if (!std::isfinite(scale)) return fail(PA_E_INVAL, "scale is not finite");
+  if (num_seqs == 0 || max_query_len == 0) return ok();
+  if (!q || !query_start || !block_tables || !context_lens || !out)
+    return fail(PA_E_INVAL, "q, query_start, block_tables, context_lens and out must be non-NULL");
+  if (static_cast<int64_t>(num_rows) * num_q_heads > 0x7fffffff)
+    return fail(PA_E_RANGE, "num_rows * num_q_heads exceeds 2^31 - 1");
+  for (const void* ptr : {q, static_cast<const void*>(out)})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+      return fail(PA_E_INVAL, "q and out must be 16-byte aligned");
+  if (num_seqs > 65535 || d.num_kv_heads > 65535)
+    return fail(PA_E_UNSUPPORTED, "more than 65535 sequences or KV heads in one call");
+  pa::PrefillArgs a;
+  a.q = q;
+  a.k_cache = pool->dev_base + static_cast<int64_t>(2 * layer) * pool->array_bytes;
+  a.v_cache = pool->dev_base + static_cast<int64_t>(2 * layer + 1) * pool->array_bytes;
+  a.query_start = query_start;
+  a.tables = block_tables;
+  a.ctx = context_lens;
+  a.out = out;
+  a.num_rows = num_rows;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = d.num_kv_heads;
+  a.max_blocks = max_blocks;
+  a.num_blocks = d.num_blocks;
+  a.block_size = d.block_size;
+  a.max_context = max_context;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(pa::launch_prefill(a, static_cast<int>(d.kv_dtype), group, max_query_len,
+                                       static_cast<hipStream_t>(stream)),
+                    "pa_prefill_chunked");
 }
 
 }  // extern "C"

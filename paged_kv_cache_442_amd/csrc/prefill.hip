@@ -1,0 +1,281 @@
+// gfx950 (CDNA4) kernel for chunked prefill over a paged KV cache.
+//
+// A long prompt is processed in chunks that are batched with decode work ("LLM inference
+// optimization: KV cache & PagedAttention", carlstack.gravito.dev, section 六 item 2;
+// "vLLM explained", jackchen890311.github.io, appendix).  The chunk's own K/V rows are
+// written into the cache first; then each query row of the chunk attends, causally, to
+// every cached token of its sequence up to and including its own position, reading
+// K/V through the block table.  Unlike decode, the query rows of a chunk form a real
+// dense contraction (prefill is a matrix product on the matrix units: carlstack page,
+// section 一.1), so QK^T and PV run on MFMA.
+//
+// Tiling.  A workgroup takes TR = 128 / G consecutive query rows of one sequence and
+// all G query heads of one KV head: 128 (row, head) columns, 32 per wave.  Keys go in
+// tiles of 32:
+//   * S^T = K Q^T with v_mfma_f32_32x32x16 (A = 32 keys x 16 dims of K from LDS, B = 16
+//     dims x 32 columns of Q held in registers).  The accumulator layout (lane l holds
+//     keys 8j + 4(l/32) + i of column l % 32) is already the B-operand layout PV needs,
+//     so probabilities never move between lanes.
+//   * Online softmax per column (the two lanes l, l ^ 32 of a column share its maximum),
+//     base 2, with the accumulators rescaled only when a score passes the reference
+//     maximum by kRescaleSlack.
+//   * O^T += V^T P^T with the same MFMA, V staged transposed in LDS.  P goes in as two
+//     MFMA operands, its bf16 (or fp16) rounding and the rounding of the remainder, so
+//     the only error left is the fp32 accumulation (a single rounding of P could move an
+//     output by several 1e-3 on rows that see only a few keys).
+//   * Causal and length masks by select; V rows past the context are zeroed when staged
+//     (a zero probability times a NaN from unused cache memory would still be NaN).
+#include <math.h>
+
+#include "prefill.hpp"
+
+namespace pa {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kHead = 128;    // head_dim
+constexpr int kKeys = 32;     // keys per tile
+constexpr int kCols = 128;    // (row, head) columns per workgroup
+constexpr int kKRow = kHead + 8;   // K tile row stride in LDS (elements), against bank conflicts
+constexpr int kVRow = kKeys + 8;   // transposed V tile row stride (elements)
+constexpr float kRescaleSlack = 8.0f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+struct MmaBF16 {
+  typedef __bf16 elem;
+  __device__ static f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+struct MmaF16 {
+  typedef _Float16 elem;
+  __device__ static f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+// Two 16-bit values packed into a dword, low half first.
+template <class T>
+__device__ __forceinline__ uint32_t pack2(T lo, T hi) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+}
+
+template <class M, int G>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
+  using T = typename M::elem;
+  constexpr int TR = kCols / G;  // query rows per workgroup
+
+  __shared__ __align__(16) T s_k[kKeys * kKRow];   // K tile, [key][dim]
+  __shared__ __align__(16) T s_vt[kHead * kVRow];  // V tile transposed, [dim][key]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int half = lane / 32;  // which 8 of a 16-dim slice, which 4 keys of 8
+  const int seq = blockIdx.y;
+  const int kvh = blockIdx.z;
+  const int r0 = blockIdx.x * TR;
+
+  const int qs = a.query_start[seq];
+  const int n_rows = a.query_start[seq + 1] - qs;
+  if (r0 >= n_rows) return;  // wave-uniform: the whole workgroup leaves
+  const int L = a.ctx[seq];
+  const bool bad = L < 0 || L > a.max_context ||
+                   static_cast<int64_t>(L) > static_cast<int64_t>(a.max_blocks) * a.block_size ||
+                   n_rows > L || qs < 0 || qs + n_rows > a.num_rows;
+
+  // This lane's column: wave w holds columns 32w .. 32w + 31; column n is query head
+  // n / TR of the group, row r0 + n % TR of the sequence's chunk.
+  const int col = wave * 32 + (lane % 32);
+  const int hh = col / TR;
+  const int row = r0 + col % TR;
+  const bool col_ok = row < n_rows;
+  const int pos = L - n_rows + row;  // the row's position; it sees keys 0 .. pos
+  const int64_t out_row = (static_cast<int64_t>(qs) + row) * a.num_q_heads + kvh * G + hh;
+
+  if (bad) {
+    if (col_ok && !(qs < 0 || qs + n_rows > a.num_rows)) {
+#pragma unroll
+      for (int d4 = 0; d4 < kHead; d4 += 8)
+        *reinterpret_cast<f32x4*>(a.out + out_row * kHead + d4 + 4 * half) =
+            f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+    return;
+  }
+
+  // Q^T operands: slice s covers dims 16s .. 16s + 15; lane l holds dims 16s + 8 half ..
+  // + 7 of its column.
+  u32x4 qb[8];
+  {
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + out_row * kHead);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qb[s] = col_ok ? qrow[2 * s + half] : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // Largest key any column of the workgroup sees.
+  const int kmax = L - n_rows + min(r0 + TR, n_rows) - 1;
+  const int n_tiles = kmax / kKeys + 1;
+
+  // Staging: thread t moves 16-byte chunk t % 16 of keys 2 (t / 16) and 2 (t / 16) + 1.
+  const int sc = tid % 16;
+  const int sk = 2 * (tid / 16);
+  const int32_t* tbl = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+  const int64_t row_elems = kHead;
+  const int64_t run_elems = static_cast<int64_t>(a.block_size) * kHead;
+  bool bad_blk = false;
+  u32x4 kst[2], vst[2];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = t0 + sk + j;
+      kst[j] = vst[j] = u32x4{0u, 0u, 0u, 0u};
+      if (t <= kmax) {
+        int phys = tbl[t / a.block_size];
+        if (static_cast<unsigned>(phys) >= static_cast<unsigned>(a.num_blocks)) {
+          bad_blk = true;
+          phys = 0;
+        }
+        const int64_t off = (static_cast<int64_t>(phys) * a.num_kv_heads + kvh) * run_elems +
+                            static_cast<int64_t>(t % a.block_size) * row_elems + sc * 8;
+        kst[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.k_cache) + off);
+        vst[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.v_cache) + off);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&s_k[(sk + j) * kKRow + sc * 8]) = kst[j];
+    // V transposed: dims sc * 8 .. + 7, keys sk and sk + 1 side by side.
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a0 = vst[0][w], a1 = vst[1][w];
+      const int d = sc * 8 + 2 * w;
+      *reinterpret_cast<uint32_t*>(&s_vt[d * kVRow + sk]) = (a0 & 0xffffu) | (a1 << 16);
+      *reinterpret_cast<uint32_t*>(&s_vt[(d + 1) * kVRow + sk]) = (a0 >> 16) | (a1 & 0xffff0000u);
+    }
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+  float m_ref = -INFINITY;  // reference maximum of this lane's column (base 2)
+  float l_part = 0.0f;      // sum of this lane's probabilities (its 16 keys of each tile)
+
+  load_tile(0);
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int t0 = tile * kKeys;
+    __syncthreads();  // the previous tile's reads of the LDS tiles are done
+    store_tile();
+    __syncthreads();
+    if (tile + 1 < n_tiles) load_tile(t0 + kKeys);
+
+    // S^T for 32 keys x this wave's 32 columns.
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(&s_k[(lane % 32) * kKRow + 16 * sl + 8 * half]);
+      s = M::mma(ka, qb[sl], s);
+    }
+
+    // Scores in base 2, masked; lane holds keys t0 + 8j + 4 half + i, j, i = 0..3.
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = t0 + 8 * (r / 4) + 4 * half + (r % 4);
+      const float z = (col_ok && key <= pos) ? s[r] * a.scale_log2 : -INFINITY;
+      s[r] = z;
+      tmax = fmaxf(tmax, z);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // the column's other 16 keys
+    if (tmax > m_ref + kRescaleSlack) {
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - tmax);  // 0 on the first tile
+      m_ref = tmax;
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    }
+    // Probabilities, split into a 16-bit value and the 16-bit rounding of the rest.
+    uint32_t ph[8], pl[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = col_ok ? __builtin_amdgcn_exp2f(s[r] - m_ref) : 0.0f;
+      const float p1 = col_ok ? __builtin_amdgcn_exp2f(s[r + 1] - m_ref) : 0.0f;
+      l_part += p0 + p1;
+      const T h0 = static_cast<T>(p0), h1 = static_cast<T>(p1);
+      const T e0 = static_cast<T>(p0 - static_cast<float>(h0));
+      const T e1 = static_cast<T>(p1 - static_cast<float>(h1));
+      ph[r / 2] = pack2(h0, h1);
+      pl[r / 2] = pack2(e0, e1);
+    }
+    // O^T += V^T P^T: MFMA q covers keys 16q .. 16q + 15; its B operand is this lane's
+    // probabilities 8q .. 8q + 7, whose keys (in operand order) are 16q + 4 half + i and
+    // 16q + 8 + 4 half + i, i = 0..3.
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4 bh = u32x4{ph[4 * q], ph[4 * q + 1], ph[4 * q + 2], ph[4 * q + 3]};
+      const u32x4 bl = u32x4{pl[4 * q], pl[4 * q + 1], pl[4 * q + 2], pl[4 * q + 3]};
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const T* vrow = &s_vt[(32 * dt + lane % 32) * kVRow + 16 * q + 4 * half];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+        const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
+        o[dt] = M::mma(va, bh, o[dt]);
+        o[dt] = M::mma(va, bl, o[dt]);
+      }
+    }
+  }
+
+  // A block id outside the pool anywhere in the workgroup's keys makes every output NaN.
+  bad_blk = __syncthreads_or(bad_blk);
+  if (!col_ok) return;
+  const float l_col = l_part + __shfl_xor(l_part, 32);
+  const float inv = bad_blk ? __builtin_nanf("") : 1.0f / l_col;
+  // Lane holds dims 32 dt + 8 j + 4 half + i of its column.
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v = f32x4{o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2], o[dt][4 * j + 3]} * inv;
+      *reinterpret_cast<f32x4*>(a.out + out_row * kHead + 32 * dt + 8 * j + 4 * half) = v;
+    }
+}
+
+template <class M>
+hipError_t launch_typed(const PrefillArgs& a, int group, dim3 grid, hipStream_t s) {
+  switch (group) {
+    case 1: hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_kernel<M, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_kernel<M, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_kernel<M, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_kernel<M, 8>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int group, int max_query_len,
+                          hipStream_t s) {
+  (void)hipGetLastError();
+  const int tr = kCols / group;
+  const dim3 grid(static_cast<unsigned>((max_query_len + tr - 1) / tr),
+                  static_cast<unsigned>(a.num_seqs), static_cast<unsigned>(a.num_kv_heads));
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  switch (dtype) {
+    case 1: return launch_typed<MmaF16>(a, group, grid, s);
+    case 2: return launch_typed<MmaBF16>(a, group, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -131,3 +131,105 @@ class DecodeSession:
         base = 2 * self.layer * per
         shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
         return flat[base:base + per].view(shape), flat[base + per:base + 2 * per].view(shape)
+
+
+class PrefillSession:
+    """A mixed batch: prefill chunks over cached prefixes plus single-token decode rows.
+
+    Every sequence's tokens (prefix, chunk, decode history) get blocks from the block
+    manager and are written to their slots.  One step then rewrites the chunk rows and
+    the decode rows' newest tokens (``pa_reshape_and_cache``), runs the chunks through
+    ``pa_prefill_chunked`` and the decode rows through ``pa_decode``.
+    """
+
+    def __init__(self, w, device="cuda", partition_tokens=0, poison=True, chunk_tokens=1 << 16):
+        self.w = w
+        self.device = device
+        self.partition_tokens = partition_tokens
+        self.desc = pa.make_desc(1, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype)
+        self.storage = torch.empty(pa.pa_pool_bytes(self.desc), dtype=torch.uint8, device=device)
+        if poison:
+            nan_fill(self.storage, w.dtype)
+        self.pool = pa.pa_alloc_pool(self.desc, self.storage, w.free_order)
+        lens = w.seq_lens()
+        self.n_chunks = len(w.chunk_lens)
+        self.n_decode = len(w.decode_lens)
+        self.seqs = [pa.pa_seq_new(self.pool) for _ in range(len(lens))]
+        slots = [pa.pa_seq_append(self.pool, s, int(L))[0] if L > 0 else np.zeros(0, np.int64)
+                 for s, L in zip(self.seqs, lens)]
+        offs = w.token_offsets
+        all_rows = np.arange(offs[-1])
+        all_slots = np.concatenate(slots) if slots else np.zeros(0, np.int64)
+        for a in range(0, len(all_rows), chunk_tokens):
+            idx = all_rows[a:a + chunk_tokens]
+            pa.pa_reshape_and_cache(self.pool, 0, bits_to_device(w.k_tokens[idx], w.dtype, device),
+                                    bits_to_device(w.v_tokens[idx], w.dtype, device),
+                                    torch.from_numpy(all_slots[a:a + chunk_tokens]).to(device))
+        torch.cuda.synchronize()
+
+        # The step's writes: each chunk's rows and each decode row's newest token.
+        step_rows, step_slots = [], []
+        for i in range(self.n_chunks):
+            c = int(w.chunk_lens[i])
+            step_rows.append(np.arange(offs[i + 1] - c, offs[i + 1]))
+            step_slots.append(slots[i][len(slots[i]) - c:])
+        for j in range(self.n_decode):
+            s = self.n_chunks + j
+            if lens[s] > 0:
+                step_rows.append(np.array([offs[s + 1] - 1]))
+                step_slots.append(slots[s][-1:])
+        rows = np.concatenate(step_rows) if step_rows else np.zeros(0, np.int64)
+        self.step_k = bits_to_device(w.k_tokens[rows], w.dtype, device)
+        self.step_v = bits_to_device(w.v_tokens[rows], w.dtype, device)
+        self.step_slots = torch.from_numpy(np.concatenate(step_slots) if step_slots
+                                           else np.zeros(0, np.int64)).to(device)
+
+        def tables_of(seqs):
+            mb = max(1, max((-(-pa.pa_seq_length(self.pool, s) // w.block_size) for s in seqs),
+                            default=1))
+            t, c = pa.pa_export_block_tables(self.pool, seqs, mb)
+            return t, c
+
+        chunk_seqs = self.seqs[:self.n_chunks]
+        dec_seqs = self.seqs[self.n_chunks:]
+        tc, cc = tables_of(chunk_seqs)
+        self.tables_c_host, self.ctx_c_host = tc, cc
+        self.tables_c = torch.from_numpy(tc).to(device)
+        self.ctx_c = torch.from_numpy(cc).to(device)
+        self.max_ctx_c = int(cc.max()) if len(cc) else 0
+        qs = np.concatenate([[0], np.cumsum(np.asarray(w.chunk_lens, dtype=np.int64))]).astype(np.int32)
+        self.query_start = torch.from_numpy(qs).to(device)
+        self.max_query_len = int(np.max(w.chunk_lens)) if self.n_chunks else 0
+        self.q_c = bits_to_device(w.q_chunks, w.dtype, device)
+        self.out_c = torch.empty(int(qs[-1]), w.num_q_heads, w.head_dim, dtype=torch.float32,
+                                 device=device)
+        td, cd = tables_of(dec_seqs) if dec_seqs else (np.zeros((0, 1), np.int32), np.zeros(0, np.int32))
+        self.tables_d_host, self.ctx_d_host = td, cd
+        self.tables_d = torch.from_numpy(td).to(device)
+        self.ctx_d = torch.from_numpy(cd).to(device)
+        self.max_ctx_d = int(cd.max()) if len(cd) else 0
+        self.q_d = bits_to_device(w.q_decode, w.dtype, device)
+        self.out_d = torch.empty(self.n_decode, w.num_q_heads, w.head_dim, dtype=torch.float32,
+                                 device=device)
+        ws = pa.pa_decode_workspace_bytes(self.pool, self.n_decode, w.num_q_heads, self.max_ctx_d,
+                                          partition_tokens)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        self.scale = 1.0 / math.sqrt(w.head_dim)
+
+    def write_step_tokens(self, stream=None):
+        pa.pa_reshape_and_cache(self.pool, 0, self.step_k, self.step_v, self.step_slots, stream)
+
+    def prefill(self, stream=None):
+        pa.pa_prefill_chunked(self.pool, 0, self.q_c, self.query_start, self.tables_c, self.ctx_c,
+                              self.max_ctx_c, self.max_query_len, self.scale, self.out_c, stream)
+
+    def decode(self, stream=None):
+        if self.n_decode:
+            pa.pa_decode(self.pool, 0, self.q_d, self.tables_d, self.ctx_d, self.max_ctx_d,
+                         self.scale, self.out_d, self.workspace, self.partition_tokens, stream)
+
+    def step(self, stream=None):
+        self.write_step_tokens(stream)
+        self.prefill(stream)
+        self.decode(stream)
+

@@ -263,3 +263,25 @@ def chunked_prefill(seed=5, num_chunks=8, min_chunk=256, max_chunk=512, max_pref
     return ChunkedPrefillWorkload(dtype, num_q_heads, num_kv_heads, head_dim, block_size, N,
                                   prefix_lens, chunk_lens, decode_lens, perm, q_chunks, q_decode,
                                   k, v)
+
+
+def custom_chunked(seed, dtype, prefix_lens, chunk_lens, decode_lens, num_q_heads, num_kv_heads,
+                   head_dim=128, block_size=16, num_blocks=None):
+    """Any chunked-prefill shape: the given prefixes and chunks, plus decode rows."""
+    rng = np.random.default_rng(seed)
+    chunk_lens = np.asarray(chunk_lens, dtype=np.int64)
+    prefix_lens = np.asarray(prefix_lens, dtype=np.int64)
+    decode_lens = np.asarray(decode_lens, dtype=np.int64)
+    lens = np.concatenate([prefix_lens + chunk_lens, decode_lens])
+    if num_blocks is None:
+        num_blocks = max(1, math.ceil(1.25 * sum(_blocks(L, block_size) for L in lens)))
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    q_chunks = _normal_bits(rng, (int(chunk_lens.sum()), num_q_heads, head_dim), dtype)
+    q_decode = _normal_bits(rng, (len(decode_lens), num_q_heads, head_dim), dtype)
+    total = int(lens.sum())
+    k = _normal_bits(rng, (total, num_kv_heads, head_dim), dtype)
+    v = _normal_bits(rng, (total, num_kv_heads, head_dim), dtype)
+    return ChunkedPrefillWorkload(dtype, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                  prefix_lens, chunk_lens, decode_lens, perm, q_chunks, q_decode,
+                                  k, v)
+

@@ -1,0 +1,144 @@
+"""GPU parity for chunked prefill (``pa_prefill_chunked``) against the float64 CPU oracle.
+
+Every expected value comes from the workload's own token-ordered K/V: the oracle's
+decode of a row at position p over tokens 0..p is causal attention for that row.
+Tolerance: 2e-3 max abs error (fp16/bf16 inputs, fp32 accumulation).
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, fpbits
+from paged_kv_cache_442_amd import binding as pa
+from paged_kv_cache_442_amd import workloads as wl
+from paged_kv_cache_442_amd.session import PrefillSession
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def announce(msg):
+    print("\n[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def seq_tokens(w, s):
+    a, b = w.token_offsets[s], w.token_offsets[s + 1]
+    return fpbits.decode(w.dtype, w.k_tokens[a:b]), fpbits.decode(w.dtype, w.v_tokens[a:b])
+
+
+def oracle_chunk_row(w, i, r, kv_cache=None):
+    """Chunk i, its row r: attention over tokens 0 .. prefix + r of sequence i."""
+    kc, vc = kv_cache if kv_cache is not None else seq_tokens(w, i)
+    pos = int(w.prefix_lens[i]) + r
+    q = w.q_chunks[int(w.chunk_offsets[i]) + r]
+    return attention.contiguous_decode(w.dtype, q, kc[:pos + 1], vc[:pos + 1],
+                                       attention.default_scale(w.head_dim))
+
+
+def check_chunks(sess, rows_of):
+    w = sess.w
+    got = sess.out_c.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for i in range(sess.n_chunks):
+        kv = seq_tokens(w, i)
+        for r in rows_of(i):
+            want = oracle_chunk_row(w, i, r, kv)
+            row = got[int(w.chunk_offsets[i]) + r]
+            assert np.isfinite(row).all(), f"non-finite output, chunk {i} row {r}"
+            worst = max(worst, float(np.max(np.abs(row - want))))
+    assert worst <= TOL, f"max abs error {worst:.3e}"
+    return worst
+
+
+PREFIXES = [0, 0, 5, 100, 33, 700]
+CHUNKS = [1, 40, 17, 160, 64, 300]
+
+
+@pytest.mark.parametrize("dtype,H_q,H_kv,bs", [
+    (wl.BF16, 32, 8, 32), (wl.BF16, 32, 8, 16), (wl.BF16, 8, 8, 16), (wl.BF16, 16, 8, 32),
+    (wl.BF16, 64, 8, 16), (wl.F16, 32, 8, 32), (wl.F16, 8, 4, 16),
+])
+def test_prefill_small_shapes_all_rows(dtype, H_q, H_kv, bs):
+    announce(f"prefill dtype={dtype} H_q={H_q} H_kv={H_kv} bs={bs}")
+    w = wl.custom_chunked(200 + H_q + bs, dtype, PREFIXES, CHUNKS, [], H_q, H_kv, block_size=bs)
+    sess = PrefillSession(w)
+    sess.step()
+    torch.cuda.synchronize()
+    check_chunks(sess, lambda i: range(int(w.chunk_lens[i])))
+
+
+def test_prefill_single_rows_equal_the_decode_oracle():
+    """A one-row chunk is a decode row: the same numbers as the oracle's decode."""
+    announce("prefill with one-row chunks")
+    w = wl.custom_chunked(7, wl.BF16, [0, 15, 16, 255, 1000], [1, 1, 1, 1, 1], [], 32, 8, block_size=32)
+    sess = PrefillSession(w)
+    sess.step()
+    torch.cuda.synchronize()
+    check_chunks(sess, lambda i: [0])
+
+
+def sampled_rows(w, i, rng):
+    c = int(w.chunk_lens[i])
+    rows = {0, 1, 2, c - 2, c - 1} | set(int(x) for x in rng.integers(0, c, size=6))
+    return sorted(r for r in rows if 0 <= r < c)
+
+
+def test_mixed_batch_full_size_sampled():
+    """The mixed chunked-prefill + decode batch at full size (GQA 32/8, bf16, block 32)."""
+    announce("mixed batch full size: 8 chunks over prefixes + 96 decode rows")
+    w = wl.chunked_prefill()
+    sess = PrefillSession(w)
+    sess.step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    check_chunks(sess, lambda i: sampled_rows(w, i, rng))
+    got = sess.out_d.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    worst = 0.0
+    for j in sorted(set(int(x) for x in rng.integers(0, sess.n_decode, size=8)) | {0}):
+        s = sess.n_chunks + j
+        kc, vc = seq_tokens(w, s)
+        want = attention.contiguous_decode(w.dtype, w.q_decode[j], kc, vc,
+                                           attention.default_scale(w.head_dim))
+        worst = max(worst, float(np.max(np.abs(got[j] - want))))
+    assert worst <= TOL, worst
+
+
+def test_invalid_sequences_get_nan_and_nothing_else_changes():
+    announce("prefill: bad table id, more rows than context")
+    w = wl.custom_chunked(9, wl.BF16, [40, 40, 40], [20, 20, 20], [], 16, 4, block_size=16)
+    sess = PrefillSession(w)
+    sess.prefill()
+    good = sess.out_c.clone()
+    tables = sess.tables_c.clone()
+    ctx = sess.ctx_c.clone()
+    tables[0, 1] = w.num_blocks + 3        # a key block outside the pool
+    ctx[1] = 10                            # 20 query rows but only 10 tokens
+    out = torch.full_like(sess.out_c, 5.0)
+    pa.pa_prefill_chunked(sess.pool, 0, sess.q_c, sess.query_start, tables, ctx, sess.max_ctx_c,
+                          sess.max_query_len, sess.scale, out)
+    torch.cuda.synchronize()
+    qs = sess.query_start.cpu().numpy()
+    assert torch.isnan(out[qs[0]:qs[1]]).all()
+    assert torch.isnan(out[qs[1]:qs[2]]).all()
+    assert torch.equal(out[qs[2]:qs[3]], good[qs[2]:qs[3]])
+
+
+def test_fp32_cache_is_rejected():
+    announce("prefill on an fp32 cache -> unsupported")
+    desc = pa.make_desc(1, 4, 16, 2, 128, pa.F32)
+    storage = torch.zeros(pa.pa_pool_bytes(desc), dtype=torch.uint8, device="cuda")
+    pool = pa.pa_alloc_pool(desc, storage)
+    q = torch.zeros(1, 2, 128, dtype=torch.float32, device="cuda")
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_prefill_chunked(pool, 0, q, torch.tensor([0, 1], dtype=torch.int32, device="cuda"),
+                              torch.zeros(1, 1, dtype=torch.int32, device="cuda"),
+                              torch.ones(1, dtype=torch.int32, device="cuda"), 1, 1,
+                              1 / math.sqrt(128), torch.zeros_like(q))
+    assert e.value.code == pa.PA_E_UNSUPPORTED
