@@ -2,7 +2,8 @@
 
 A step is one decode step of one layer over the whole batch: the newest token of
 every sequence is written into its slot (``pa_reshape_and_cache``), then
-``pa_decode`` runs its two kernels (per-partition attention, log-sum-exp merge).
+``pa_decode`` runs its three kernels (the work plan, the per-partition attention, the
+log-sum-exp merge of partitions).
 Inputs (pool, tables, queries) are resident in HBM before timing starts.
 
 The JSON line reports:

@@ -100,6 +100,7 @@ int64_t items_bytes(int64_t num_seqs, int64_t pmax) {
   return (num_seqs * pmax * 16 + 255) / 256 * 256;
 }
 
+
 struct DecodeCall {
   pa::DecodeArgs args;
   int group;
@@ -450,8 +451,8 @@ int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs, int
                           workspace_bytes, stream);
   if (st) return st;
   st = pa_decode_partitions(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
-                                context_lens, max_context, scale, partition_tokens, out, workspace,
-                                workspace_bytes, stream);
+                            context_lens, max_context, scale, partition_tokens, out, workspace,
+                            workspace_bytes, stream);
   if (st) return st;
   return pa_decode_reduce(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
                           context_lens, max_context, scale, partition_tokens, out, workspace,
