@@ -239,8 +239,7 @@ def main():
     for s, L in zip(hseqs, lens):
         pa.pa_seq_append(hp, s, int(L) - 1)
     t0 = time.perf_counter()
-    for s in hseqs:
-        pa.pa_seq_append(hp, s, 1)
+    pa.pa_seq_append_batch(hp, hseqs)      # one scheduling step: one token per sequence
     host_mgr_us = (time.perf_counter() - t0) * 1e6
 
     blocks = sum(-(-int(L) // w.block_size) for L in lens)

@@ -125,6 +125,17 @@ int pa_pool_layer_ptrs(const pa_pool* pool, int32_t layer, void** k_base, void**
 int pa_seq_new(pa_pool* pool, int32_t* seq_out);
 int pa_seq_append(pa_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots_out,
                   int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out);
+/* pa_seq_append_batch: one scheduling step's appends in one call: n_tokens[i] tokens
+ *                (n_tokens == NULL: one each) to seqs[i] (host, `count` distinct live
+ *                ids), in that order, with exactly the effect of consecutive
+ *                pa_seq_append calls, but all-or-nothing for the whole batch
+ *                (PA_E_NOMEM / PA_E_RANGE / PA_E_INVAL leave the manager unchanged).
+ *                slots_out (host) receives the slots back to back, in batch order;
+ *                cow_pairs_out (host, 2 * cow_cap) the copy-on-write pairs in batch
+ *                order, their count in *n_cow_out. */
+int pa_seq_append_batch(pa_pool* pool, const int32_t* seqs, int32_t count, const int32_t* n_tokens,
+                        int64_t* slots_out, int32_t* cow_pairs_out, int32_t cow_cap,
+                        int32_t* n_cow_out);
 int pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* child_out);
 int pa_seq_free(pa_pool* pool, int32_t seq);
 int pa_seq_length(const pa_pool* pool, int32_t seq, int32_t* len_out);

@@ -50,6 +50,7 @@ _SIGNATURES = {
     "pa_pool_layer_ptrs": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
     "pa_seq_new": (ctypes.c_int, [_P, _PI32]),
     "pa_seq_append": (ctypes.c_int, [_P, _I32, _I32, _PI64, _PI32, _I32, _PI32]),
+    "pa_seq_append_batch": (ctypes.c_int, [_P, _PI32, _I32, _PI32, _PI64, _PI32, _I32, _PI32]),
     "pa_seq_fork": (ctypes.c_int, [_P, _I32, _PI32]),
     "pa_seq_free": (ctypes.c_int, [_P, _I32]),
     "pa_seq_length": (ctypes.c_int, [_P, _I32, _PI32]),
@@ -199,6 +200,23 @@ def pa_seq_append(pool, seq, n_tokens):
     _check(lib().pa_seq_append(pool.handle, seq, n_tokens, slots.ctypes.data_as(_PI64),
                                _i32p(pairs), 1, ctypes.byref(n_cow)))
     return slots[:n_tokens], [(int(pairs[0]), int(pairs[1]))] if n_cow.value else []
+
+
+def pa_seq_append_batch(pool, seqs, n_tokens=None):
+    """Returns ``(slots int64[sum n], cow_pairs list of (src, dst))`` for the whole batch."""
+    seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+    counts = np.ones(len(seqs), np.int32) if n_tokens is None else \
+        np.ascontiguousarray(n_tokens, dtype=np.int32)
+    total = int(counts.sum())
+    slots = np.zeros(max(1, total), dtype=np.int64)
+    cap = max(1, len(seqs))
+    pairs = np.zeros(2 * cap, dtype=np.int32)
+    n_cow = ctypes.c_int32()
+    _check(lib().pa_seq_append_batch(pool.handle, _i32p(seqs), len(seqs),
+                                     None if n_tokens is None else _i32p(counts),
+                                     slots.ctypes.data_as(_PI64), _i32p(pairs), cap,
+                                     ctypes.byref(n_cow)))
+    return slots[:total], [(int(pairs[2 * i]), int(pairs[2 * i + 1])) for i in range(n_cow.value)]
 
 
 def pa_seq_fork(pool, parent):

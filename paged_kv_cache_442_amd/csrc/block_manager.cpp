@@ -67,6 +67,48 @@ MgrStatus BlockManager::seq_append(int32_t seq, int32_t n, int64_t* slots, int32
   return MgrStatus::ok;
 }
 
+MgrStatus BlockManager::seq_append_batch(const int32_t* seqs, int32_t count, const int32_t* n,
+                                         int64_t* slots, int32_t* cow_pairs, int32_t cow_cap,
+                                         int32_t* n_cow) {
+  // Work out what the whole batch takes before changing anything: copies depend on
+  // reference counts that earlier copies in the batch lower.
+  std::unordered_map<int32_t, int32_t> dropped;  // block -> references given up so far
+  std::unordered_map<int32_t, char> seen;
+  int64_t need = 0, copies = 0;
+  const int64_t bs = block_size_;
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t s = seqs[i];
+    const int32_t k = n ? n[i] : 1;
+    if (!live(s) || k < 0 || seen.count(s)) return MgrStatus::invalid;
+    seen[s] = 1;
+    const Seq& q = seqs_[s];
+    const int64_t L = q.length;
+    if (L + k > INT32_MAX) return MgrStatus::range;
+    if (k > 0 && L % bs != 0) {
+      const int32_t last = q.table.back();
+      if (refcount_[last] - dropped[last] > 1) {
+        ++dropped[last];
+        ++copies;
+      }
+    }
+    need += (L + k + bs - 1) / bs - (L + bs - 1) / bs;
+  }
+  if (copies > cow_cap) return MgrStatus::range;
+  if (need + copies > static_cast<int64_t>(free_stack_.size())) return MgrStatus::no_blocks;
+
+  int32_t made = 0;
+  int64_t at = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t k = n ? n[i] : 1;
+    int32_t c = 0;
+    seq_append(seqs[i], k, slots + at, cow_pairs + 2 * made, cow_cap - made, &c);
+    made += c;
+    at += k;
+  }
+  *n_cow = made;
+  return MgrStatus::ok;
+}
+
 MgrStatus BlockManager::seq_fork(int32_t parent, int32_t* child) {
   if (!live(parent)) return MgrStatus::invalid;
   int32_t id;

@@ -16,6 +16,7 @@
 
 #include <cstdint>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 namespace pa {
@@ -32,6 +33,12 @@ class BlockManager {
   // Appends n tokens.  On success writes n slots and at most one copy-on-write pair.
   MgrStatus seq_append(int32_t seq, int32_t n, int64_t* slots, int32_t* cow_pairs,
                        int32_t cow_cap, int32_t* n_cow);
+  // Appends n[i] tokens (n == nullptr: one each) to seqs[0..count) in that order, as
+  // consecutive seq_append calls would, but all-or-nothing for the whole batch.  Slots
+  // are written back to back; at most one copy-on-write pair per sequence.  A sequence
+  // may appear only once.
+  MgrStatus seq_append_batch(const int32_t* seqs, int32_t count, const int32_t* n, int64_t* slots,
+                             int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow);
   MgrStatus seq_fork(int32_t parent, int32_t* child);
   MgrStatus seq_free(int32_t seq);
 

@@ -283,6 +283,22 @@ int pa_seq_append(pa_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots_o
   return st;
 }
 
+int pa_seq_append_batch(pa_pool* pool, const int32_t* seqs, int32_t count, const int32_t* n_tokens,
+                        int64_t* slots_out, int32_t* cow_pairs_out, int32_t cow_cap,
+                        int32_t* n_cow_out) {
+  if (!pool || !n_cow_out) return fail(PA_E_INVAL, "pool and n_cow_out must be non-NULL");
+  if (count < 0 || (count > 0 && (!seqs || !slots_out)))
+    return fail(PA_E_INVAL, "bad seqs / count / slots_out");
+  if (cow_cap < 0 || (cow_cap > 0 && !cow_pairs_out)) return fail(PA_E_INVAL, "bad cow_pairs_out / cow_cap");
+  int32_t dummy_pair[2];
+  int32_t* pairs = cow_cap > 0 ? cow_pairs_out : dummy_pair;
+  int32_t n_cow = 0;
+  int st = mgr_status(pool->mgr->seq_append_batch(seqs, count, n_tokens, slots_out, pairs, cow_cap, &n_cow),
+                      "pa_seq_append_batch");
+  if (st == PA_OK) *n_cow_out = n_cow;
+  return st;
+}
+
 int pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* child_out) {
   if (!pool || !child_out) return fail(PA_E_INVAL, "pool and child_out must be non-NULL");
   return mgr_status(pool->mgr->seq_fork(parent, child_out), "pa_seq_fork");

@@ -184,3 +184,58 @@ def test_append_out_of_blocks_changes_nothing():
     assert pa.pa_seq_length(p, c) == 6
     slots, pairs = pa.pa_seq_append(p, c, 2)      # CoW only
     assert len(pairs) == 1 and len(slots) == 2
+
+
+def test_batch_append_equals_sequential_appends():
+    """One batched step == the same appends one by one, through the Python model."""
+    rng = random.Random(5)
+    p = host_pool(200, 4, list(range(199, -1, -1)))
+    model = BlockManagerModel(200, 4, list(range(199, -1, -1)))
+    roots = []
+    for _ in range(6):
+        s = pa.pa_seq_new(p)
+        m = model.seq_new()
+        assert s == m
+        n = rng.randint(1, 13)
+        pa.pa_seq_append(p, s, n)
+        model.seq_append(m, n)
+        roots.append(s)
+    for r in roots[:3]:                      # shared partial blocks -> copies in the batch
+        for _ in range(2):
+            c = pa.pa_seq_fork(p, r)
+            assert c == model.seq_fork(r)
+    for step in range(5):
+        order = list(range(12))
+        rng.shuffle(order)
+        counts = [rng.randint(0, 5) for _ in order]
+        slots, pairs = pa.pa_seq_append_batch(p, order, counts)
+        want_slots, want_pairs = [], []
+        for s, k in zip(order, counts):
+            sl, pr = model.seq_append(s, k)
+            want_slots += list(sl)
+            want_pairs += pr
+        assert slots.tolist() == want_slots
+        assert pairs == want_pairs
+        tables, ctx = pa.pa_export_block_tables(p, order, 64)
+        for i, s in enumerate(order):
+            assert tables[i][:len(model.table(s))].tolist() == model.table(s)
+            assert ctx[i] == model.length(s)
+        assert pa.pa_export_free_stack(p).tolist() == model.free_stack_top_first()
+
+
+def test_batch_append_is_all_or_nothing():
+    p = host_pool(4, 4)
+    a, b = pa.pa_seq_new(p), pa.pa_seq_new(p)
+    pa.pa_seq_append(p, a, 3)
+    pa.pa_seq_append(p, b, 4)
+    before = pa.pa_export_free_stack(p).tolist()
+    with pytest.raises(pa.PAError) as ei:
+        pa.pa_seq_append_batch(p, [a, b], [2, 9])    # a needs 1 block, b needs 3: 4 > 2 free
+    assert ei.value.code == pa.PA_E_NOMEM
+    assert pa.pa_export_free_stack(p).tolist() == before
+    assert pa.pa_seq_length(p, a) == 3 and pa.pa_seq_length(p, b) == 4
+    with pytest.raises(pa.PAError) as ei:
+        pa.pa_seq_append_batch(p, [a, a])
+    assert ei.value.code == pa.PA_E_INVAL
+    slots, pairs = pa.pa_seq_append_batch(p, [b, a])
+    assert len(slots) == 2 and pairs == []
