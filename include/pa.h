@@ -226,6 +226,27 @@ int pa_decode_reduce(pa_pool* pool, int32_t layer, const void* q, int32_t num_se
                      int32_t partition_tokens, float* out, void* workspace,
                      int64_t workspace_bytes, void* stream);
 
+/* Sliding-window decode: pa_decode in which sequence s attends only to its last
+ *   `window` tokens, [max(0, L_s - window), L_s) ("vLLM explained", table of when KV may be
+ *   overwritten: with a sliding-window model the KV outside the window can be dropped).
+ *   window == 0 is plain pa_decode.  Table entries of blocks wholly before a sequence's
+ *   window are never read, so they may be -1 (see pa_seq_release_before).  Arguments,
+ *   workspace and errors as for pa_decode (PA_E_INVAL for window < 0). */
+int pa_decode_window(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
+                     int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                     const int32_t* context_lens, int32_t max_context, int32_t window, float scale,
+                     int32_t partition_tokens, float* out, void* workspace, int64_t workspace_bytes,
+                     void* stream);
+
+/* pa_seq_release_before: the sliding window of `seq` has moved past `token`: every block
+ *   whose tokens all lie before `token` (block j with (j + 1) * block_size <= token),
+ *   except the sequence's last block, loses this sequence's reference (going back on
+ *   the free stack, in logical order, when no holder is left) and its table entry
+ *   becomes -1.  The length does not change; appends and forks work as before (a fork
+ *   shares the holes).  *n_released_out = entries cleared now.  PA_E_INVAL for an
+ *   unknown sequence or token < 0. */
+int pa_seq_release_before(pa_pool* pool, int32_t seq, int32_t token, int32_t* n_released_out);
+
 /* Chunked prefill of one layer: causal attention of the query rows of several
  *   sequences, each over that sequence's paged cache ("LLM inference optimization: KV
  *   cache & PagedAttention", carlstack.gravito.dev, section 六 item 2: long prompts in

@@ -177,3 +177,13 @@ def lse_merge(parts):
     W = [l * math.exp(m - M) for m, l, _ in live]
     num = sum(w * o for w, (_, _, o) in zip(W, live))
     return num / sum(W)
+
+
+def window_decode(dtype, q_bits, k_contig, v_contig, scale, window):
+    """Decode over the last ``window`` tokens of a sequence (0 = all of them): with a
+    sliding-window model only those tokens are attended ("vLLM explained", table of when
+    KV may be overwritten).  ``k_contig, v_contig``: float64 ``[L][num_kv_heads][d]``."""
+    L = k_contig.shape[0]
+    start = max(0, L - window) if window > 0 else 0
+    return contiguous_decode(dtype, q_bits, k_contig[start:], v_contig[start:], scale)
+

@@ -114,18 +114,44 @@ class BlockManagerModel:
         self.tables[child] = list(self.tables[parent])
         self.lengths[child] = self.lengths[parent]
         for blk in self.tables[child]:
-            self.refcount[blk] += 1
+            if blk >= 0:
+                self.refcount[blk] += 1
         return child
 
     def seq_free(self, seq):
         if seq not in self.tables:
             raise KeyError(seq)
         for blk in self.tables[seq]:
+            if blk < 0:
+                continue
             self.refcount[blk] -= 1
             if self.refcount[blk] == 0:
                 self.stack.append(blk)
         del self.tables[seq]
         del self.lengths[seq]
+
+    def seq_release_before(self, seq, token):
+        """A sliding window has moved past ``token``: drop this sequence's hold on every
+        block whose tokens all come before it ("vLLM explained", table of when KV may be
+        overwritten: KV outside a sliding window can be dropped).  The last block is
+        always kept (it holds the newest token).  Dropped entries become -1.  Returns the
+        number of entries dropped now."""
+        if seq not in self.tables or token < 0:
+            raise KeyError(seq)
+        table = self.tables[seq]
+        dropped = 0
+        for j in range(len(table) - 1):
+            if (j + 1) * self.block_size > token:
+                break
+            blk = table[j]
+            if blk < 0:
+                continue
+            self.refcount[blk] -= 1
+            if self.refcount[blk] == 0:
+                self.stack.append(blk)
+            table[j] = -1
+            dropped += 1
+        return dropped
 
     def export_tables(self, seqs, max_blocks):
         """``(tables, context_lens)``: ``[n][max_blocks]`` padded with -1, and lengths."""
@@ -144,7 +170,8 @@ class BlockManagerModel:
         held = {}
         for row in self.tables.values():
             for blk in row:
-                held[blk] = held.get(blk, 0) + 1
+                if blk >= 0:
+                    held[blk] = held.get(blk, 0) + 1
         for blk in range(self.num_blocks):
             assert self.refcount[blk] == held.get(blk, 0), blk
         free = set(self.stack)

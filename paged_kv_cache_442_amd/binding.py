@@ -67,6 +67,9 @@ _SIGNATURES = {
     "pa_decode_reduce": (ctypes.c_int, _DECODE_ARGS),
     "pa_prefill_chunked": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _I32,
                                           _I32, ctypes.c_float, _P, _P]),
+    "pa_decode_window": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _I32,
+                                        ctypes.c_float, _I32, _P, _P, _I64, _P]),
+    "pa_seq_release_before": (ctypes.c_int, [_P, _I32, _I32, _PI32]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 
@@ -340,3 +343,25 @@ def pa_prefill_chunked(pool, layer, q, query_start, block_tables, context_lens, 
                                     _dev(context_lens, torch.int32, "context_lens"), max_context,
                                     max_query_len, float(scale), _dev(out, torch.float32, "out"),
                                     _stream(stream)))
+
+
+def pa_decode_window(pool, layer, q, block_tables, context_lens, max_context, window, scale, out,
+                     workspace, partition_tokens=0, stream=None):
+    """Decode over each sequence's last ``window`` tokens (0 = all)."""
+    import torch
+    S, H_q = q.shape[0], q.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_window(pool.handle, layer, _dev(q, torch_dtype(pool.desc.kv_dtype), "q"), S,
+                                  H_q, _dev(block_tables, torch.int32, "block_tables"),
+                                  block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens"),
+                                  max_context, window, float(scale), partition_tokens,
+                                  _dev(out, torch.float32, "out"),
+                                  None if workspace is None else _dev(workspace, name="workspace"),
+                                  ws_bytes, _stream(stream)))
+
+
+def pa_seq_release_before(pool, seq, token):
+    n = ctypes.c_int32()
+    _check(lib().pa_seq_release_before(pool.handle, seq, token, ctypes.byref(n)))
+    return n.value
+

@@ -1,6 +1,8 @@
 // Host block manager (see block_manager.hpp for the rules and their sources).
 #include "block_manager.hpp"
 
+#include <algorithm>
+
 namespace pa {
 
 BlockManager::BlockManager(int32_t num_blocks, int32_t block_size,
@@ -109,6 +111,24 @@ MgrStatus BlockManager::seq_append_batch(const int32_t* seqs, int32_t count, con
   return MgrStatus::ok;
 }
 
+MgrStatus BlockManager::seq_release_before(int32_t seq, int32_t token, int32_t* released) {
+  if (!live(seq) || token < 0) return MgrStatus::invalid;
+  Seq& s = seqs_[seq];
+  // Block j holds tokens [j * bs, (j + 1) * bs); it is wholly before `token` when
+  // (j + 1) * bs <= token.  The last block of a sequence stays whatever `token` is.
+  const int64_t whole = std::min<int64_t>(token / block_size_, static_cast<int64_t>(s.table.size()) - 1);
+  int32_t n = 0;
+  for (int64_t j = 0; j < whole; ++j) {
+    const int32_t b = s.table[j];
+    if (b < 0) continue;
+    if (--refcount_[b] == 0) free_stack_.push_back(b);
+    s.table[j] = -1;
+    ++n;
+  }
+  *released = n;
+  return MgrStatus::ok;
+}
+
 MgrStatus BlockManager::seq_fork(int32_t parent, int32_t* child) {
   if (!live(parent)) return MgrStatus::invalid;
   int32_t id;
@@ -118,7 +138,8 @@ MgrStatus BlockManager::seq_fork(int32_t parent, int32_t* child) {
   const Seq& p = seqs_[parent];  // re-read: seq_new may have moved the vector
   c.table = p.table;
   c.length = p.length;
-  for (int32_t b : c.table) refcount_[b] += 1;
+  for (int32_t b : c.table)
+    if (b >= 0) refcount_[b] += 1;
   *child = id;
   return MgrStatus::ok;
 }
@@ -127,7 +148,7 @@ MgrStatus BlockManager::seq_free(int32_t seq) {
   if (!live(seq)) return MgrStatus::invalid;
   Seq& s = seqs_[seq];
   for (int32_t b : s.table) {
-    if (--refcount_[b] == 0) free_stack_.push_back(b);
+    if (b >= 0 && --refcount_[b] == 0) free_stack_.push_back(b);
   }
   s.live = false;
   s.length = 0;

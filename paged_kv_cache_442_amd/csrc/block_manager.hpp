@@ -41,6 +41,9 @@ class BlockManager {
                              int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow);
   MgrStatus seq_fork(int32_t parent, int32_t* child);
   MgrStatus seq_free(int32_t seq);
+  // Releases every block of seq whose tokens all lie before `token` (a sliding window
+  // that has moved past them); their table entries become -1.  Sets *released.
+  MgrStatus seq_release_before(int32_t seq, int32_t token, int32_t* released);
 
   bool live(int32_t seq) const;
   int32_t length(int32_t seq) const { return seqs_[seq].length; }

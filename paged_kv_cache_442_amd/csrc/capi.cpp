@@ -110,7 +110,8 @@ int prepare_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs
                    int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
                    const int32_t* context_lens, int32_t max_context, float scale,
                    int32_t partition_tokens, float* out, void* workspace, int64_t workspace_bytes,
-                   DecodeCall* call) {
+                   DecodeCall* call, int32_t window = 0) {
+  if (window < 0) return fail(PA_E_INVAL, "window %d < 0", window);
   int st = check_device_pool(pool, layer);
   if (st) return st;
   const pa_pool_desc& d = pool->desc;
@@ -179,6 +180,7 @@ int prepare_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs
   a.max_context = max_context;
   a.partition_tokens = partition_tokens;
   a.pmax = static_cast<int32_t>(pmax);
+  a.window = window;
   a.scale_log2 = scale * 1.4426950408889634f;
   call->group = group;
   return PA_OK;
@@ -533,4 +535,34 @@ int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_
                     "pa_prefill_chunked");
 }
 
+int pa_decode_window(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
+                     int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                     const int32_t* context_lens, int32_t max_context, int32_t window, float scale,
+                     int32_t partition_tokens, float* out, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
+  DecodeCall c;
+  int st = prepare_decode(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+                          context_lens, max_context, scale, partition_tokens, out, workspace,
+                          workspace_bytes, &c, window);
+  if (st) return st;
+  if (c.args.num_seqs == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(pa::launch_decode_plan(c.args, s), "pa_decode_window (plan)");
+  if (st) return st;
+  st = hip_status(pa::launch_decode_partitions(c.args, static_cast<int>(pool->desc.kv_dtype), c.group, s),
+                  "pa_decode_window (partitions)");
+  if (st) return st;
+  if (c.args.pmax <= 1) return ok();
+  return hip_status(pa::launch_decode_reduce(c.args, s), "pa_decode_window (reduce)");
+}
+
+int pa_seq_release_before(pa_pool* pool, int32_t seq, int32_t token, int32_t* n_released_out) {
+  if (!pool || !n_released_out) return fail(PA_E_INVAL, "pool and n_released_out must be non-NULL");
+  int32_t n = 0;
+  int st = mgr_status(pool->mgr->seq_release_before(seq, token, &n), "pa_seq_release_before");
+  if (st == PA_OK) *n_released_out = n;
+  return st;
+}
+
 }  // extern "C"
+

@@ -210,6 +210,15 @@ __device__ __forceinline__ T ld_uniform(const T* p, int64_t i) {
   return ((const __attribute__((address_space(4))) T*)(p))[i];
 }
 
+// First token a sequence of length L attends to (a sliding window of `window` tokens;
+// 0 = no window), and the tile-aligned token its first partition starts at.
+__device__ __forceinline__ int window_start(int L, int window) {
+  return window > 0 && L > window ? L - window : 0;
+}
+__device__ __forceinline__ int window_base(int L, int window) {
+  return window_start(L, window) / kTileTokens * kTileTokens;
+}
+
 // Log-sum-exp merge of one query row's n partitions, dims d4 .. d4 + 3:
 //   M = max_p lse_p,  w_p = 2^(lse_p - M),  out = sum_p w_p o_p / sum_p w_p,
 // where o_p is partition p's normalized output and lse_p its base-2 log-sum-exp (the
@@ -299,12 +308,15 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     return u.L < 0 || u.L > a.max_context ||
            static_cast<int64_t>(u.L) > static_cast<int64_t>(a.max_blocks) * a.block_size;
   };
+  // Partition `part` covers tokens [t_begin, t_end): partitions start at the window's
+  // tile-aligned first token.
+  auto t_begin_of = [&](const Unit& u) { return window_base(u.L, a.window) + u.part * P; };
   auto t_end_of = [&](const Unit& u) {
-    return (is_bad(u) || u.L == 0) ? u.part * P : min(u.L, u.part * P + P);
+    return (is_bad(u) || u.L == 0) ? t_begin_of(u) : min(u.L, t_begin_of(u) + P);
   };
   // Number of tiles this wave takes in a unit (tiles stream, stream + NS, ...).
   auto wave_tiles = [&](const Unit& u) {
-    const int n_tiles = (t_end_of(u) - u.part * P + kTileTokens - 1) / kTileTokens;
+    const int n_tiles = (t_end_of(u) - t_begin_of(u) + kTileTokens - 1) / kTileTokens;
     return stream < n_tiles ? (n_tiles - stream + NS - 1) / NS : 0;
   };
   // Row offset (rows of head_dim elements from the layer's K base) of the wave's tile
@@ -312,7 +324,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
   // tiles.  partition_tokens <= kMaxPartition keeps a wave's tiles within 64 lanes.
   auto tile_rows = [&](const Unit& u, int nt) -> int {
     if (lane >= nt) return 0;
-    const int t0 = u.part * P + (stream + NS * lane) * kTileTokens;
+    const int t0 = t_begin_of(u) + (stream + NS * lane) * kTileTokens;
     const int phys = a.tables[static_cast<int64_t>(u.seq) * a.max_blocks + t0 / a.block_size];
     if (static_cast<unsigned>(phys) >= static_cast<unsigned>(a.num_blocks)) return -1;
     return (phys * a.num_kv_heads + u.kvh) * a.block_size + t0 % a.block_size;
@@ -367,8 +379,9 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     const bool has_next = nxt < n_work;
     const Unit nx = unit_of(has_next ? nxt : cur);
     const int nt_nx = has_next ? wave_tiles(nx) : 0;
-    const int t_begin = it.part * P;
+    const int t_begin = t_begin_of(it);
     const int t_end = t_end_of(it);
+    const int t_lo = window_start(it.L, a.window);  // tokens before it are outside the window
 
     u32x4 qv[GW];
     {
@@ -452,7 +465,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
       for (int i = 0; i < LOADS; ++i) {
         pin(s[i][0]);
         const int t = t0 + i * TG + rr;
-        z[i] = t < t_end ? s[i][0] * a.scale_log2 : -INFINITY;
+        z[i] = (t < t_end && t >= t_lo) ? s[i][0] * a.scale_log2 : -INFINITY;
       }
       __builtin_amdgcn_sched_barrier(0);
 
@@ -481,7 +494,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
         }
       }
 
-      const bool partial_tile = t0 + kTileTokens > t_end;
+      const bool partial_tile = t0 + kTileTokens > t_end || t0 < t_lo;
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const float pr = __builtin_amdgcn_exp2f(z[i] - m_ref);
@@ -490,8 +503,9 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
 #pragma unroll
         for (int w = 0; w < 4; ++w) E::widen(vr[i][w], &v[w * (VD / 4)]);
         if (partial_tile) {
-          // Rows past the context may hold anything (even NaN): drop them by select.
-          const bool keep = t0 + i * TG + rr < t_end;
+          // Rows past the context (or before the window) may hold anything, even NaN:
+          // drop them by select.
+          const bool keep = t0 + i * TG + rr < t_end && t0 + i * TG + rr >= t_lo;
 #pragma unroll
           for (int e = 0; e < VD; ++e) {
             pin(v[e]);
@@ -552,7 +566,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
               f32x4{o[h][e4], o[h][e4 + 1], o[h][e4 + 2], o[h][e4 + 3]};
       __syncthreads();
 
-      const int n_parts = (it.L + P - 1) / P;
+      const int n_parts = (it.L - window_base(it.L, a.window) + P - 1) / P;
       for (int idx = tid; idx < G * (kHeadDim / 4); idx += blockDim.x) {
         const int h = idx / (kHeadDim / 4);
         const int d4 = (idx % (kHeadDim / 4)) * 4;
@@ -634,8 +648,9 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeA
       *full = 0;
       *partial = 1;
     } else {
-      *full = L / P;
-      *partial = (L % P) != 0;
+      const int span = L - window_base(L, a.window);  // tokens from the first partition on
+      *full = span / P;
+      *partial = (span % P) != 0;
     }
   };
   // Pass 1: the number of full items (the partial items are listed after them).
@@ -696,7 +711,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeArgs a) 
   if (L <= 0 || L > a.max_context ||
       static_cast<int64_t>(L) > static_cast<int64_t>(a.max_blocks) * a.block_size)
     return;  // written (zeros or NaN) by the partition kernel
-  const int n = (L + a.partition_tokens - 1) / a.partition_tokens;
+  const int n = (L - window_base(L, a.window) + a.partition_tokens - 1) / a.partition_tokens;
   if (n <= 1) return;  // written by the partition kernel
   const int d4 = (threadIdx.x % 32) * 4;
   *reinterpret_cast<f32x4*>(a.out + row * kHeadDim + d4) = merge_partitions(a, row, n, d4);

@@ -31,6 +31,7 @@ struct DecodeArgs {
   int32_t* work_items;      // [S * pmax][4] (sequence, partition, context length, 0)
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks, num_blocks, block_size;
   int32_t max_context, partition_tokens, pmax;
+  int32_t window;           // attend to the last `window` tokens only; 0 = all
   float scale_log2;         // scale * log2(e)
 };
 
