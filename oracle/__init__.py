@@ -17,11 +17,14 @@ Contents (each function cites the page passage it follows):
                        log-sum-exp merge of partitions.
 * ``cache_ops``     -- slot-mapped K/V writes and whole-block copies as bit copies.
 * ``block_manager`` -- a pure-Python model of the block manager (free list,
-                       reference counts, block tables, copy-on-write).
+                       reference counts, block tables, copy-on-write, release of
+                       blocks behind a sliding window).
+* ``fp8``           -- exact decoding of e4m3 codes and quantization (scale, clamp,
+                       round to nearest even) for an FP8 KV cache.
 
 Every function here is pinned by ``-m "not gpu"`` tests to facts fixed by the
 pages and by mathematics (closed forms, special cases, brute force); none is
 marked "parity unpinned".
 """
 
-from . import fpbits, sizes, attention, cache_ops, block_manager  # noqa: F401
+from . import fpbits, sizes, attention, cache_ops, block_manager, fp8  # noqa: F401
