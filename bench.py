@@ -37,15 +37,17 @@ WORKLOADS = {
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def algorithmic_bytes(w, window=0):
-    """K+V read once per (sequence, KV head) plus Q: sum_s L_s*H_kv*d*2*e + S*H_q*d*e
-    (with a sliding window, L_s counts only the tokens inside the window)."""
-    e = 4 if w.dtype == 0 else 2
+def algorithmic_bytes(w, window=0, kv_bytes=None):
+    """K+V read once per (sequence, KV head) plus Q: sum_s L_s*H_kv*d*2*e + S*H_q*d*e_q
+    (with a sliding window, L_s counts only the tokens inside the window; an FP8 cache
+    has e = 1 for K/V and bf16 queries)."""
+    eq = 4 if w.dtype == 0 else 2
+    e = eq if kv_bytes is None else kv_bytes
     lens = np.asarray(w.context_lens, dtype=np.int64)
     if window:
         lens = np.minimum(lens, window)
     kv = int(np.sum(lens)) * w.num_kv_heads * w.head_dim * 2 * e
-    q = w.num_seqs * w.num_q_heads * w.head_dim * e
+    q = w.num_seqs * w.num_q_heads * w.head_dim * eq
     return kv + q
 
 
@@ -155,6 +157,8 @@ def main():
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--num-q-heads", type=int, default=0,
                     help="diagnostic: query heads of the llama3_70b shape (default 64)")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="keep K/V in an FP8 (e4m3) cache (bf16 workloads)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window decode over the last W tokens (pa_decode_window)")
     ap.add_argument("--fixed-len", type=int, default=0,
@@ -187,10 +191,10 @@ def main():
     print("[bench] workload %s drawn in %.1f s" % (args.workload, time.perf_counter() - t0),
           file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    sess = DecodeSession(w, partition_tokens=args.partition)
+    sess = DecodeSession(w, partition_tokens=args.partition, cache_fp8=args.kv_fp8)
     print("[bench] cache written in %.1f s" % (time.perf_counter() - t0), file=sys.stderr, flush=True)
 
-    B = algorithmic_bytes(w, args.window)
+    B = algorithmic_bytes(w, args.window, 1 if args.kv_fp8 else None)
     stream = torch.cuda.current_stream()
     if args.window:
         return bench_window(args, torch, pa, sess, w, B, stream)
@@ -233,10 +237,18 @@ def main():
     got = sess.out.cpu().numpy().astype(np.float64)
     lens = np.asarray(w.context_lens)
     worst = 0.0
+    def cache_values(bits, scale):
+        x = fpbits.decode(w.dtype, bits)
+        if not args.kv_fp8:
+            return x
+        from oracle import fp8
+        codes = fp8.quantize(x.astype(np.float32), np.float32(1.0) / np.float32(scale))
+        return fp8.dequantize(codes, scale)
+
     for s in sorted({int(np.argmin(lens)), int(np.argmax(lens))}):
         kt, vt = w.seq_tokens(s)
-        want = attention.contiguous_decode(w.dtype, w.q[s], fpbits.decode(w.dtype, kt),
-                                           fpbits.decode(w.dtype, vt),
+        want = attention.contiguous_decode(w.dtype, w.q[s], cache_values(kt, sess.k_scale),
+                                           cache_values(vt, sess.v_scale),
                                            attention.default_scale(w.head_dim))
         worst = max(worst, float(np.max(np.abs(got[s] - want))))
 
@@ -268,7 +280,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == wl.BF16 else ("f16" if w.dtype == wl.F16 else "f32"),
+        "dtype": "fp8-e4m3 kv, bf16 q" if args.kv_fp8 else
+                 ("bf16" if w.dtype == wl.BF16 else ("f16" if w.dtype == wl.F16 else "f32")),
         "data": "synthetic (seeded N(0,1) K/V/Q, seeded block permutation)",
         "config": {
             "workload": args.workload,
@@ -278,6 +291,7 @@ def main():
             "total_context_tokens": int(lens.sum()), "max_context": int(lens.max()),
             "partition_tokens": args.partition or 512,
             "block_placement": "contiguous" if args.contiguous_blocks else "seeded permutation",
+            "kv_cache": "fp8-e4m3" if args.kv_fp8 else "same as q",
             "algorithmic_bytes_per_step": B,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -47,7 +47,12 @@ enum {
   PA_E_RANGE = -5        /* an output buffer or capacity is too small                    */
 };
 
-enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
+/* Cache element types.  PA_FP8_E4M3 is the OCP 8-bit float (1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, largest magnitude 448, no infinities): a KV cache of one
+ * byte per value ("vLLM explained", block-size section: FP8 takes 1 byte; appendix:
+ * quantization shrinks the KV cache).  Its rows come in, and its queries are given, as
+ * bf16; each layer holds a K and a V scale (pa_pool_set_kv_scales). */
+enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 };
 
 typedef struct {
   int32_t num_layers;   /* >= 1                                   */
@@ -55,7 +60,7 @@ typedef struct {
   int32_t block_size;   /* tokens per block, >= 1                 */
   int32_t num_kv_heads; /* >= 1                                   */
   int32_t head_dim;     /* >= 1 (the attention kernels need 128)  */
-  int32_t kv_dtype;     /* PA_F32, PA_F16 or PA_BF16              */
+  int32_t kv_dtype;     /* PA_F32, PA_F16, PA_BF16 or PA_FP8_E4M3 */
 } pa_pool_desc;
 
 typedef struct pa_pool pa_pool; /* opaque, host-side, owned by the library */
@@ -84,6 +89,14 @@ int pa_alloc_pool(const pa_pool_desc* desc, void* dev_base, int64_t dev_bytes,
                   const int32_t* initial_free_order, pa_pool** out);
 int pa_free_pool(pa_pool* pool);
 int pa_pool_layer_ptrs(const pa_pool* pool, int32_t layer, void** k_base, void** v_base);
+
+/* pa_pool_set_kv_scales: per-tensor scales of layer `layer` (both finite and > 0; 1 by
+ *   default).  For an FP8 cache a stored code c stands for decode(c) * scale:
+ *   pa_reshape_and_cache stores round_to_nearest_even(clamp(x * (1/scale), -448, 448))
+ *   with x * (1/scale) computed in float32 (NaN stays NaN), and pa_decode /
+ *   pa_decode_window multiply scores by k_scale and outputs by v_scale.  The scales are
+ *   read at each call (host state); other dtypes ignore them. */
+int pa_pool_set_kv_scales(pa_pool* pool, int32_t layer, float k_scale, float v_scale);
 
 /* ---------------------------------------------------------------- block manager (host)
  * The KV cache is cut into fixed-size blocks that need not be contiguous; a block
@@ -188,7 +201,8 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
  * not depend on which physical blocks hold the data: the summation order follows
  * logical token order only.  Calls that share one workspace must not overlap.
  *
- *   q            device [num_seqs][num_q_heads][head_dim], pool dtype, contiguous
+ *   q            device [num_seqs][num_q_heads][head_dim], pool dtype (bf16 for an FP8
+ *                cache), contiguous
  *   block_tables device int32 [num_seqs][max_blocks]; entries past a sequence's last
  *                block are never read
  *   context_lens device int32 [num_seqs], 0 <= context_lens[s] <= max_context
@@ -202,7 +216,7 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
  * A sequence whose length exceeds max_context or max_blocks * block_size, or whose
  * table holds an id outside [0, num_blocks), gets NaN outputs; nothing outside the
  * pool is read.  Supported: head_dim 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
- * any block_size that is a multiple of 16; all three dtypes (fp32 accumulation). */
+ * any block_size that is a multiple of 16; all dtypes (fp32 accumulation). */
 int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context, int32_t partition_tokens);
 int pa_decode_plan(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,

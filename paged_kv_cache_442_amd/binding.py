@@ -11,7 +11,7 @@ import os
 
 import numpy as np
 
-F32, F16, BF16 = 0, 1, 2
+F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
 
 PA_OK, PA_E_INVAL, PA_E_NOMEM, PA_E_HIP, PA_E_UNSUPPORTED, PA_E_RANGE = 0, -1, -2, -3, -4, -5
 
@@ -48,6 +48,7 @@ _SIGNATURES = {
     "pa_alloc_pool": (ctypes.c_int, [ctypes.POINTER(PoolDesc), _P, _I64, _PI32, ctypes.POINTER(_P)]),
     "pa_free_pool": (ctypes.c_int, [_P]),
     "pa_pool_layer_ptrs": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
+    "pa_pool_set_kv_scales": (ctypes.c_int, [_P, _I32, ctypes.c_float, ctypes.c_float]),
     "pa_seq_new": (ctypes.c_int, [_P, _PI32]),
     "pa_seq_append": (ctypes.c_int, [_P, _I32, _I32, _PI64, _PI32, _I32, _PI32]),
     "pa_seq_append_batch": (ctypes.c_int, [_P, _PI32, _I32, _PI32, _PI64, _PI32, _I32, _PI32]),
@@ -120,8 +121,11 @@ def _dev(t, dtype=None, name="tensor"):
 
 
 def torch_dtype(kv_dtype):
+    """dtype of the rows and queries the library takes for a cache of ``kv_dtype`` (an
+    FP8 cache takes bf16 and quantizes on the way in)."""
     import torch
-    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[kv_dtype]
+    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16,
+            FP8_E4M3: torch.bfloat16}[kv_dtype]
 
 
 class Pool:
@@ -187,6 +191,10 @@ def pa_pool_layer_ptrs(pool, layer):
     k, v = ctypes.c_void_p(), ctypes.c_void_p()
     _check(lib().pa_pool_layer_ptrs(pool.handle, layer, ctypes.byref(k), ctypes.byref(v)))
     return k.value, v.value
+
+
+def pa_pool_set_kv_scales(pool, layer, k_scale, v_scale):
+    _check(lib().pa_pool_set_kv_scales(pool.handle, layer, float(k_scale), float(v_scale)))
 
 
 def pa_seq_new(pool):

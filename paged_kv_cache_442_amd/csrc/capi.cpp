@@ -23,6 +23,7 @@ struct pa_pool {
   int64_t dev_bytes;
   int64_t elem_bytes;
   int64_t array_bytes;  // one layer's K (or V): num_blocks * heads * block_size * head_dim * elem
+  std::vector<float> k_scale, v_scale;  // per layer (FP8 caches; 1 by default)
   std::unique_ptr<pa::BlockManager> mgr;
 };
 
@@ -47,6 +48,7 @@ int64_t elem_bytes_of(int32_t dtype) {
     case PA_F32: return 4;
     case PA_F16: return 2;
     case PA_BF16: return 2;
+    case PA_FP8_E4M3: return 1;
     default: return 0;
   }
 }
@@ -181,7 +183,8 @@ int prepare_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs
   a.partition_tokens = partition_tokens;
   a.pmax = static_cast<int32_t>(pmax);
   a.window = window;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale * pool->k_scale[layer] * 1.4426950408889634f;
+  a.v_scale = pool->v_scale[layer];
   call->group = group;
   return PA_OK;
 }
@@ -246,6 +249,8 @@ int pa_alloc_pool(const pa_pool_desc* desc, void* dev_base, int64_t dev_bytes,
   int64_t per_array_block;
   array_block_bytes(desc, &per_array_block);
   p->array_bytes = per_array_block * desc->num_blocks;
+  p->k_scale.assign(desc->num_layers, 1.0f);
+  p->v_scale.assign(desc->num_layers, 1.0f);
   p->mgr.reset(new (std::nothrow) pa::BlockManager(desc->num_blocks, desc->block_size, order));
   if (!p->mgr) return fail(PA_E_NOMEM, "host allocation failed");
   *out = p.release();
@@ -377,6 +382,16 @@ int pa_reshape_and_cache(pa_pool* pool, int32_t layer, const void* k, const void
   void *kc, *vc;
   pa_pool_layer_ptrs(pool, layer, &kc, &vc);
   const int64_t num_slots = static_cast<int64_t>(pool->desc.num_blocks) * pool->desc.block_size;
+  if (pool->desc.kv_dtype == PA_FP8_E4M3) {
+    if (pool->desc.head_dim != pa::kHeadDim)
+      return fail(PA_E_UNSUPPORTED, "FP8 cache writes need head_dim %d", pa::kHeadDim);
+    return hip_status(pa::launch_reshape_and_cache_fp8(k, v, slots, kc, vc, n_tokens,
+                                                       pool->desc.num_kv_heads, pool->desc.block_size,
+                                                       num_slots, 1.0f / pool->k_scale[layer],
+                                                       1.0f / pool->v_scale[layer],
+                                                       static_cast<hipStream_t>(stream)),
+                      "pa_reshape_and_cache");
+  }
   return hip_status(pa::launch_reshape_and_cache(k, v, slots, kc, vc, n_tokens, pool->desc.num_kv_heads,
                                                  pool->desc.block_size, num_slots,
                                                  static_cast<int32_t>(row_bytes),
@@ -562,6 +577,17 @@ int pa_seq_release_before(pa_pool* pool, int32_t seq, int32_t token, int32_t* n_
   int st = mgr_status(pool->mgr->seq_release_before(seq, token, &n), "pa_seq_release_before");
   if (st == PA_OK) *n_released_out = n;
   return st;
+}
+
+int pa_pool_set_kv_scales(pa_pool* pool, int32_t layer, float k_scale, float v_scale) {
+  if (!pool) return fail(PA_E_INVAL, "pool is NULL");
+  if (layer < 0 || layer >= pool->desc.num_layers)
+    return fail(PA_E_INVAL, "layer %d outside [0, %d)", layer, pool->desc.num_layers);
+  if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_E_INVAL, "scales must be finite and > 0");
+  pool->k_scale[layer] = k_scale;
+  pool->v_scale[layer] = v_scale;
+  return ok();
 }
 
 }  // extern "C"

@@ -20,6 +20,7 @@ namespace {
 constexpr int kWave = 64;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -34,19 +35,27 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr int kWaitVmcnt0 = 0x0F70;
 
 // ------------------------------------------------------------------ element formats
-// Each format says how one dword of q meets one dword of k (fp32-accumulated dot
-// product) and how a dword of v widens to fp32.
+// Each format says how a lane's chunk of a K/V row is loaded (Chunk: the lane's kElems
+// elements), how one dword of q meets one dword of k (fp32-accumulated dot product;
+// k_operand turns a K chunk into those dwords) and how a V chunk widens to fp32.  The
+// query is stored with kQBytes per element.
 struct ElemF32 {
-  static constexpr int kBytes = 4;
+  using Chunk = u32x4;
+  static constexpr int kBytes = 4, kQBytes = 4, kElems = 4;
   __device__ static float dot(uint32_t q, uint32_t k, float acc) {
     return fmaf(__uint_as_float(q), __uint_as_float(k), acc);
   }
   __device__ static float dot0(uint32_t q, uint32_t k) { return __uint_as_float(q) * __uint_as_float(k); }
-  __device__ static void widen(uint32_t w, float* out) { out[0] = __uint_as_float(w); }
+  __device__ static u32x4 k_operand(Chunk c) { return c; }
+  __device__ static void widen(Chunk c, float (&v)[kElems]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v[w] = __uint_as_float(c[w]);
+  }
 };
 
 struct ElemF16 {
-  static constexpr int kBytes = 2;
+  using Chunk = u32x4;
+  static constexpr int kBytes = 2, kQBytes = 2, kElems = 8;
   __device__ static float dot(uint32_t q, uint32_t k, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q), __builtin_bit_cast(f16x2, k),
                                   acc, false);
@@ -58,15 +67,20 @@ struct ElemF16 {
     asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(q), "v"(k));
     return r;
   }
-  __device__ static void widen(uint32_t w, float* out) {
-    const f16x2 h = __builtin_bit_cast(f16x2, w);
-    out[0] = static_cast<float>(h[0]);
-    out[1] = static_cast<float>(h[1]);
+  __device__ static u32x4 k_operand(Chunk c) { return c; }
+  __device__ static void widen(Chunk c, float (&v)[kElems]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f16x2 h = __builtin_bit_cast(f16x2, c[w]);
+      v[2 * w] = static_cast<float>(h[0]);
+      v[2 * w + 1] = static_cast<float>(h[1]);
+    }
   }
 };
 
 struct ElemBF16 {
-  static constexpr int kBytes = 2;
+  using Chunk = u32x4;
+  static constexpr int kBytes = 2, kQBytes = 2, kElems = 8;
   __device__ static float dot(uint32_t q, uint32_t k, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q),
                                            __builtin_bit_cast(bf16x2, k), acc, false);
@@ -76,9 +90,43 @@ struct ElemBF16 {
     asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(q), "v"(k));
     return r;
   }
-  __device__ static void widen(uint32_t w, float* out) {
-    out[0] = __uint_as_float(w << 16);
-    out[1] = __uint_as_float(w & 0xffff0000u);
+  __device__ static u32x4 k_operand(Chunk c) { return c; }
+  __device__ static void widen(Chunk c, float (&v)[kElems]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      v[2 * w] = __uint_as_float(c[w] << 16);
+      v[2 * w + 1] = __uint_as_float(c[w] & 0xffff0000u);
+    }
+  }
+};
+
+// FP8 (e4m3) cache, bf16 queries: a lane loads 8 bytes (8 elements) of a row, so a
+// 128-element row is still 16 lanes and the decode layout is the 16-bit one.  e4m3
+// values are exact in bf16 and in fp32, so K goes through the bf16 dot product and V
+// through fp32 FMAs without rounding; the per-tensor scales are applied outside.
+struct ElemFP8 {
+  using Chunk = u32x2;
+  static constexpr int kBytes = 1, kQBytes = 2, kElems = 8;
+  __device__ static float dot(uint32_t q, uint32_t k, float acc) { return ElemBF16::dot(q, k, acc); }
+  __device__ static float dot0(uint32_t q, uint32_t k) { return ElemBF16::dot0(q, k); }
+  template <bool HI>
+  __device__ static uint32_t to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  }
+  __device__ static u32x4 k_operand(Chunk c) {
+    return u32x4{to_bf16x2<false>(c.x), to_bf16x2<true>(c.x), to_bf16x2<false>(c.y),
+                 to_bf16x2<true>(c.y)};
+  }
+  __device__ static void widen(Chunk c, float (&v)[kElems]) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(c[w], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(c[w], true);
+      v[4 * w] = lo.x;
+      v[4 * w + 1] = lo.y;
+      v[4 * w + 2] = hi.x;
+      v[4 * w + 3] = hi.y;
+    }
   }
 };
 
@@ -111,8 +159,8 @@ __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 // base-2 log-sum-exp for the reduce kernel.
 template <class E, int GW>
 struct DecodeLds {
-  static constexpr int NCH = kHeadDim * E::kBytes / 16;  // 16-byte chunks per K/V row
-  static constexpr int TG = kWave / NCH;                 // rows per wave-wide 1 KiB load
+  static constexpr int NCH = kHeadDim / E::kElems;  // lane chunks per K/V row
+  static constexpr int TG = kWave / NCH;            // rows per wave-wide load
   float o[kDecodeWaves][TG][GW][kHeadDim];
   float m[kDecodeWaves][GW];
   float l[kDecodeWaves][GW];
@@ -274,9 +322,10 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
   using Lds = DecodeLds<E, GW>;
   constexpr int NCH = Lds::NCH;
   constexpr int TG = Lds::TG;
-  constexpr int LOADS = kTileTokens / TG;  // 1 KiB loads per tile (K, and again V)
-  constexpr int VD = 16 / E::kBytes;       // elements per 16-byte chunk
-  constexpr int QDW = G * kHeadDim * E::kBytes / 4;  // dwords of one group's query rows
+  constexpr int LOADS = kTileTokens / TG;  // wave-wide loads per tile (K, and again V)
+  constexpr int VD = E::kElems;            // elements per lane chunk
+  constexpr int QDW = G * kHeadDim * E::kQBytes / 4;  // dwords of one group's query rows
+  using Chunk = typename E::Chunk;
   constexpr int QPT = (QDW + kWave * kDecodeWaves - 1) / (kWave * kDecodeWaves);
   constexpr int64_t kRowBytes = kHeadDim * E::kBytes;
 
@@ -366,7 +415,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     stage_q(qd);
   }
   bool prefetched = false;  // kr / vr already hold (or are receiving) the unit's tile 0
-  u32x4 kr[LOADS], vr[LOADS];
+  Chunk kr[LOADS], vr[LOADS];
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
 
@@ -401,11 +450,11 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     // A block id outside the pool (row offset -1) makes the unit's result NaN; such
     // tiles are read from block 0 instead, so nothing outside the pool is touched.
     const bool bad_blk = __builtin_amdgcn_ballot_w64(lane < nt && rows_cur < 0) != 0;
-    auto issue = [&](int n, const char* base, u32x4 (&r)[LOADS]) {
+    auto issue = [&](int n, const char* base, Chunk (&r)[LOADS]) {
       int rows = (n >= nt && cross) ? __builtin_amdgcn_readlane(rows_next, 0)
                                     : __builtin_amdgcn_readlane(rows_cur, min(n, nt - 1));
       rows = max(rows, 0);
-      const u32x4* src = reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(rows) * kRowBytes) + lane;
+      const Chunk* src = reinterpret_cast<const Chunk*>(base + static_cast<int64_t>(rows) * kRowBytes) + lane;
 #pragma unroll
       // K and V are read once per decode step: streaming loads keep them from
       // displacing reusable lines (measured 3-6% faster than plain loads).
@@ -442,14 +491,16 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
       // level by level, so that no DPP step waits on the instruction just before it.
       float s[LOADS][GW];
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i)
+      for (int i = 0; i < LOADS; ++i) {
+        const u32x4 kk = E::k_operand(kr[i]);
 #pragma unroll
         for (int p = 0; p < GW; ++p) {
-          float acc = E::dot0(qv[p].x, kr[i].x);
-          acc = E::dot(qv[p].y, kr[i].y, acc);
-          acc = E::dot(qv[p].z, kr[i].z, acc);
-          s[i][p] = E::dot(qv[p].w, kr[i].w, acc);
+          float acc = E::dot0(qv[p].x, kk.x);
+          acc = E::dot(qv[p].y, kk.y, acc);
+          acc = E::dot(qv[p].z, kk.z, acc);
+          s[i][p] = E::dot(qv[p].w, kk.w, acc);
         }
+      }
       if (n == 0) load_next();
       issue(n + 1, kbase, kr);
       if constexpr (NCH == 32) {
@@ -500,8 +551,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
         const float pr = __builtin_amdgcn_exp2f(z[i] - m_ref);
         l_acc += pr;
         float v[VD];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) E::widen(vr[i][w], &v[w * (VD / 4)]);
+        E::widen(vr[i], v);
         if (partial_tile) {
           // Rows past the context (or before the window) may hold anything, even NaN:
           // drop them by select.
@@ -587,7 +637,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
           for (int r = 1; r < TG; ++r) sum += *reinterpret_cast<const f32x4*>(&lds.o[w][r][hw][d4]);
           acc += W * sum;
         }
-        const f32x4 res = acc / lt;
+        const f32x4 res = acc / lt * a.v_scale;
         const size_t row = group_row + h;
         if (n_parts == 1) {
           *reinterpret_cast<f32x4*>(a.out + row * kHeadDim + d4) = res;
@@ -740,6 +790,50 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   v_cache[dst] = v[i];
 }
 
+// FP8 cache writes: one thread per 16 stored bytes (16 elements) of a new row, read as
+// 32 bytes of bf16 input.  Each value is multiplied by the float32 reciprocal of the
+// layer's scale, clamped to the largest e4m3 magnitude (448; NaN stays NaN) and rounded
+// to nearest even by the hardware conversion.
+__device__ __forceinline__ float fp8_clamp(float y) {
+  return y != y ? y : fminf(fmaxf(y, -448.0f), 448.0f);
+}
+
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v, const int64_t* __restrict__ slots,
+    u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache, int64_t total_chunks,
+    int32_t num_kv_heads, int32_t block_size, int64_t num_slots, float inv_k, float inv_v) {
+  constexpr int kRowChunks = kHeadDim / 16;  // 16-byte chunks of a stored row
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total_chunks) return;
+  const int64_t row = i / kRowChunks;
+  const int c = static_cast<int>(i - row * kRowChunks);
+  const int64_t t = row / num_kv_heads;
+  const int h = static_cast<int>(row - t * num_kv_heads);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot - blk * block_size;
+  const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * kRowChunks + c;
+  auto quantize16 = [](u32x4 a0, u32x4 a1, float inv) -> u32x4 {
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u32x4& a = w < 2 ? a0 : a1;
+      const uint32_t x0 = a[2 * (w % 2)], x1 = a[2 * (w % 2) + 1];
+      const float e0 = fp8_clamp(__uint_as_float(x0 << 16) * inv);
+      const float e1 = fp8_clamp(__uint_as_float(x0 & 0xffff0000u) * inv);
+      const float e2 = fp8_clamp(__uint_as_float(x1 << 16) * inv);
+      const float e3 = fp8_clamp(__uint_as_float(x1 & 0xffff0000u) * inv);
+      int d = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+      d = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, d, true);
+      out[w] = static_cast<uint32_t>(d);
+    }
+    return out;
+  };
+  k_cache[dst] = quantize16(k[2 * i], k[2 * i + 1], inv_k);
+  v_cache[dst] = quantize16(v[2 * i], v[2 * i + 1], inv_v);
+}
+
 // ------------------------------------------------------------------ block copies
 // blockIdx.x = pair, blockIdx.y = array (layer * 2 + {K, V}); the workgroup copies one
 // whole block of that array (carlstack page, section 三.2: copy-on-write).
@@ -812,6 +906,7 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int dtype, int group, h
     case 0: return launch_decode_typed<ElemF32>(a, group, s);
     case 1: return launch_decode_typed<ElemF16>(a, group, s);
     case 2: return launch_decode_typed<ElemBF16>(a, group, s);
+    case 3: return launch_decode_typed<ElemFP8>(a, group, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -843,6 +938,21 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, const int64_t*
                      static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), slots,
                      static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), total,
                      num_kv_heads, block_size, num_slots, row_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, const int64_t* slots,
+                                        void* k_cache, void* v_cache, int32_t n_tokens,
+                                        int32_t num_kv_heads, int32_t block_size, int64_t num_slots,
+                                        float inv_k, float inv_v, hipStream_t s) {
+  (void)hipGetLastError();
+  const int64_t total = static_cast<int64_t>(n_tokens) * num_kv_heads * (kHeadDim / 16);
+  if (total == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  hipLaunchKernelGGL(reshape_and_cache_fp8_kernel, grid, dim3(256), 0, s,
+                     static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), slots,
+                     static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), total,
+                     num_kv_heads, block_size, num_slots, inv_k, inv_v);
   return hipGetLastError();
 }
 

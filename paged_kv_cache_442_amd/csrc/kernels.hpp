@@ -32,13 +32,15 @@ struct DecodeArgs {
   int32_t num_seqs, num_q_heads, num_kv_heads, max_blocks, num_blocks, block_size;
   int32_t max_context, partition_tokens, pmax;
   int32_t window;           // attend to the last `window` tokens only; 0 = all
-  float scale_log2;         // scale * log2(e)
+  float scale_log2;         // scale * log2(e) (times the K scale of an FP8 cache)
+  float v_scale;            // V scale of an FP8 cache (1 otherwise)
 };
 
 // The plan kernel lists the work items and zeroes the work counter; the partition
 // kernel (persistent) needs a plan on the same workspace before it.
 hipError_t launch_decode_plan(const DecodeArgs& a, hipStream_t s);
-// dtype: 0 fp32, 1 fp16, 2 bf16; group = num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+// dtype: 0 fp32, 1 fp16, 2 bf16, 3 fp8 e4m3 (bf16 queries); group = num_q_heads /
+// num_kv_heads in {1, 2, 4, 8}.
 hipError_t launch_decode_partitions(const DecodeArgs& a, int dtype, int group, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t s);
 
@@ -46,6 +48,13 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, const int64_t*
                                     void* k_cache, void* v_cache, int32_t n_tokens,
                                     int32_t num_kv_heads, int32_t block_size, int64_t num_slots,
                                     int32_t row_bytes, hipStream_t s);
+
+// FP8 cache writes from bf16 rows [n_tokens][num_kv_heads][128]; inv_k, inv_v are the
+// float32 reciprocals of the layer's scales.
+hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, const int64_t* slots,
+                                        void* k_cache, void* v_cache, int32_t n_tokens,
+                                        int32_t num_kv_heads, int32_t block_size, int64_t num_slots,
+                                        float inv_k, float inv_v, hipStream_t s);
 
 // base: pool base, holding `arrays` (= 2 * num_layers) arrays, each of num_blocks blocks of
 // block_bytes bytes (one layer's K or V part of a block).

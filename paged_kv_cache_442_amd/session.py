@@ -17,6 +17,7 @@ from . import binding as pa
 from . import workloads as wl
 
 _TORCH = {wl.F32: torch.float32, wl.F16: torch.float16, wl.BF16: torch.bfloat16}
+FP8 = pa.FP8_E4M3
 
 
 def bits_to_device(bits, dtype, device):
@@ -30,24 +31,44 @@ def bits_to_device(bits, dtype, device):
 
 def nan_fill(storage, dtype):
     """Fill a pool's bytes with the quiet-NaN pattern of its dtype."""
-    storage.view(_TORCH[dtype]).fill_(float("nan"))
+    if dtype == FP8:
+        storage.fill_(0x7F)
+    else:
+        storage.view(_TORCH[dtype]).fill_(float("nan"))
+
+
+def fp8_scale(bits, dtype):
+    """A per-tensor FP8 scale for bf16/fp16 rows: the largest magnitude maps to 448."""
+    x = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(_TORCH[dtype]).float()
+    amax = float(x.abs().max()) if x.numel() else 1.0
+    return max(amax, 1e-30) / 448.0
 
 
 class DecodeSession:
     def __init__(self, w, device="cuda", partition_tokens=0, num_layers=1, layer=0, poison=True,
-                 max_context=None, chunk_tokens=1 << 16):
+                 max_context=None, chunk_tokens=1 << 16, cache_fp8=False):
+        """``cache_fp8``: keep the (bf16) workload's K/V in an FP8 cache, with per-tensor
+        scales from the data's largest magnitude."""
         self.w = w
         self.device = device
         self.layer = layer
         self.partition_tokens = partition_tokens
         self.dtype = w.dtype
+        self.cache_dtype = FP8 if cache_fp8 else w.dtype
+        if cache_fp8 and w.dtype != wl.BF16:
+            raise ValueError("an FP8 cache takes bf16 rows")
         self.desc = pa.make_desc(num_layers, w.num_blocks, w.block_size, w.num_kv_heads,
-                                 w.head_dim, w.dtype)
+                                 w.head_dim, self.cache_dtype)
         nbytes = pa.pa_pool_bytes(self.desc)
         self.storage = torch.empty(nbytes, dtype=torch.uint8, device=device)
         if poison:
-            nan_fill(self.storage, w.dtype)
+            nan_fill(self.storage, self.cache_dtype)
         self.pool = pa.pa_alloc_pool(self.desc, self.storage, w.free_order)
+        self.k_scale = self.v_scale = 1.0
+        if cache_fp8:
+            self.k_scale = fp8_scale(w.k_tokens, w.dtype)
+            self.v_scale = fp8_scale(w.v_tokens, w.dtype)
+            pa.pa_pool_set_kv_scales(self.pool, layer, self.k_scale, self.v_scale)
         S = w.num_seqs
         lens = np.asarray(w.context_lens, dtype=np.int64)
         self.seqs = [pa.pa_seq_new(self.pool) for _ in range(S)]
@@ -124,10 +145,11 @@ class DecodeSession:
         self.decode(stream)
 
     def layer_cache(self):
-        """(K, V) of the session's layer as ``[N][H_kv][bs][d]`` tensors of the pool dtype."""
+        """(K, V) of the session's layer as ``[N][H_kv][bs][d]`` tensors of the pool dtype
+        (uint8 codes for an FP8 cache)."""
         w = self.w
         per = w.num_blocks * w.num_kv_heads * w.block_size * w.head_dim
-        flat = self.storage.view(_TORCH[w.dtype])
+        flat = self.storage if self.cache_dtype == FP8 else self.storage.view(_TORCH[w.dtype])
         base = 2 * self.layer * per
         shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
         return flat[base:base + per].view(shape), flat[base + per:base + 2 * per].view(shape)
