@@ -71,7 +71,10 @@ struct ElemF16 {
   __device__ static void widen(Chunk c, float (&v)[kElems]) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const f16x2 h = __builtin_bit_cast(f16x2, c[w]);
+      // Copy the element out first: a bit cast of the vector-element lvalue c[w] reads
+      // element 0 whatever w is (seen in the generated code).
+      const uint32_t x = c[w];
+      const f16x2 h = __builtin_bit_cast(f16x2, x);
       v[2 * w] = static_cast<float>(h[0]);
       v[2 * w + 1] = static_cast<float>(h[1]);
     }

@@ -1,12 +1,21 @@
 """The decode kernel's hand-placed DPP instructions, checked in its compiled gfx950 code.
 
-The PV step reads each probability through a DPP row broadcast inside an inline-asm
+1. The PV step reads each probability through a DPP row broadcast inside an inline-asm
 FMA, which the compiler's hazard recognizer cannot see; the kernel therefore places
 an ``s_nop 1`` after the VALU write of the probability.  Hardware requires two wait
 states between a VALU write of a VGPR and a DPP read of it, and a missing wait makes
-the FMA read a stale value.  This test compiles the kernels to assembly with the
-library's own flags and checks every DPP instruction.  It needs hipcc, not a GPU.
+the FMA read a stale value.  Every DPP instruction is checked.
+
+2. A lane's V chunk of 8 fp16 values sits in 4 dwords, and each must be widened on its
+own.  A bit cast of a vector element taken as an lvalue once made the compiler widen
+element 0 four times.  A 16-token tile is 4 wave-wide loads of 4 rows, so the fp16
+kernels must convert from 4 x 4 = 16 distinct registers (the faulty code used 4).
+
+The kernels are compiled to assembly with the library's own flags; hipcc is needed,
+not a GPU.
 """
+
+import re
 
 import os
 import shutil
@@ -18,6 +27,11 @@ from paged_kv_cache_442_amd import build
 
 pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                                 reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    return compile_to_asm(tmp_path_factory.mktemp("isa"))
 
 
 def compile_to_asm(tmp_path):
@@ -64,8 +78,8 @@ def dpp_hazards(asm):
     return total, bad
 
 
-def test_every_dpp_read_waits_two_states_after_the_write(tmp_path):
-    total, bad = dpp_hazards(compile_to_asm(tmp_path))
+def test_every_dpp_read_waits_two_states_after_the_write(asm):
+    total, bad = dpp_hazards(asm)
     assert total > 0
     assert not bad, "DPP read too soon after the VALU write: %s" % bad[:3]
 
@@ -78,3 +92,32 @@ def test_the_scan_catches_a_missing_wait():
                      "v_fmac_f32_dpp v59, v88, v80 row_newbcast:0 row_mask:0xf bank_mask:0xf"])
     total, bad = dpp_hazards(asm)
     assert total == 2 and len(bad) == 1 and "v87" in bad[0][0]
+
+
+def kernel_bodies(asm, pattern):
+    """{symbol: text} of the kernels whose symbol matches ``pattern``."""
+    starts = [(m.start(), m.group(1)) for m in re.finditer(r"^(_Z\S+):", asm, re.M)]
+    out = {}
+    for i, (pos, name) in enumerate(starts):
+        if re.search(pattern, name):
+            end = starts[i + 1][0] if i + 1 < len(starts) else len(asm)
+            out[name] = asm[pos:end]
+    return out
+
+
+def f16_widen_sources(body):
+    return {line.split()[2].rstrip(",") for line in instructions(body)
+            if line.split()[0].startswith("v_cvt_f32_f16")}
+
+
+def test_fp16_decode_widens_every_dword_of_a_chunk(asm):
+    kernels = kernel_bodies(asm, r"decode_partition_kernel.*ElemF16")
+    assert len(kernels) == 4
+    for name, body in kernels.items():
+        assert len(f16_widen_sources(body)) >= 16, name
+
+
+def test_the_widen_scan_catches_one_dword_widened_four_times():
+    body = "\n".join(["v_cvt_f32_f16_sdwa v73, v30 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1",
+                      "v_cvt_f32_f16_e32 v74, v30"] * 4)
+    assert f16_widen_sources(body) == {"v30"}
