@@ -108,7 +108,8 @@ int pa_pool_set_kv_scales(pa_pool* pool, int32_t layer, float k_scale, float v_s
  * a branch writes a different token into it (carlstack page, section 三.2).
  *
  * Rules where the pages are silent (all operations are deterministic):
- *   - Free list: a LIFO stack; freed blocks are pushed in logical order.
+ *   - Free list: a LIFO stack; freed blocks are pushed in logical order (last to
+ *     first when prefix caching is on, see below).
  *   - Append of n tokens at length L: if L % block_size != 0 and the last block's
  *     reference count is > 1, that block is first copied (copy-on-write): a fresh
  *     block p' is taken, the pair (p, p') is reported, p loses one reference and p'
@@ -155,8 +156,63 @@ int pa_seq_length(const pa_pool* pool, int32_t seq, int32_t* len_out);
 int pa_export_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n,
                            int32_t max_blocks, int32_t* tables_out, int32_t* ctx_out);
 int pa_block_refcount(const pa_pool* pool, int32_t block, int32_t* rc_out);
+/* pa_num_free_blocks: blocks an append may take (free and empty, plus free and cached
+ *                when prefix caching is on). */
 int pa_num_free_blocks(const pa_pool* pool, int32_t* n_out);
 int pa_export_free_stack(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
+
+/* ---------------------------------------------------------------- prefix caching (host)
+ * A prompt prefix that many requests share has its KV computed once and reused.  The
+ * cache is not a separate region: it lives in the same block pool.  A block is in use
+ * (reference count > 0), free and empty, or free but still holding cached content; a
+ * request that needs a block takes an empty one first and only then evicts a free
+ * cached block, least recently used first; blocks in use are never evicted ("vLLM
+ * explained", jackchen890311.github.io, section on prefix caching and its figure of
+ * the three block states).
+ *
+ * Rules where the pages are silent (deterministic, like the rest of the manager):
+ *   - Identity: a full block is identified by the token ids of its sequence from the
+ *     first token through the block's last token (exactly; no hash collisions).  Only
+ *     full blocks are cached.
+ *   - A block is registered when an append fills it, if every token of the sequence
+ *     was appended with its id (pa_seq_append_tokens / _batch_tokens; one append
+ *     without ids stops this for the rest of the sequence's life, forks included) and
+ *     no other block has that identity yet.
+ *   - pa_seq_new_prefix takes the longest run of cached blocks (in use or free) whose
+ *     identities match the prompt's leading full blocks, at most (n_prompt - 1) /
+ *     block_size of them, so at least one prompt token is left to compute.
+ *   - A block whose reference count reaches 0 goes to the most-recent end of the LRU
+ *     list if it is cached, else onto the free stack.  When prefix caching is on,
+ *     blocks released together (pa_seq_free, pa_seq_release_before) are released
+ *     from the last logical block to the first, so a sequence's tail is evicted before
+ *     its prefix.  Eviction drops the block's identity.
+ *
+ * pa_pool_enable_prefix_caching: turns prefix caching on for the pool's manager;
+ *   PA_E_INVAL while any sequence is live.  It stays on.
+ * pa_seq_new_prefix: new sequence (id in *seq_out) that shares the matching cached
+ *   blocks; *n_cached_out = tokens they cover (a multiple of block_size), which is the
+ *   new sequence's length.  prompt: host int32 [n_prompt] token ids.  The caller then
+ *   appends prompt[*n_cached_out:] with pa_seq_append_tokens, writes those tokens' K/V
+ *   and runs prefill over them only.  PA_E_INVAL if prefix caching is off.
+ * pa_seq_append_tokens / pa_seq_append_batch_tokens: pa_seq_append /
+ *   pa_seq_append_batch with the appended tokens' ids (host int32, one per appended
+ *   token, back to back in batch order).  On a pool without prefix caching the ids
+ *   are ignored.
+ * pa_block_state: 0 free and empty, 1 in use, 2 free and cached.
+ * pa_export_evictable: free cached blocks, next to be evicted first; PA_E_RANGE if
+ *   cap is too small (*n_out is still set). */
+enum { PA_BLOCK_FREE_EMPTY = 0, PA_BLOCK_IN_USE = 1, PA_BLOCK_FREE_CACHED = 2 };
+int pa_pool_enable_prefix_caching(pa_pool* pool);
+int pa_seq_new_prefix(pa_pool* pool, const int32_t* prompt, int32_t n_prompt, int32_t* seq_out,
+                      int32_t* n_cached_out);
+int pa_seq_append_tokens(pa_pool* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens,
+                         int64_t* slots_out, int32_t* cow_pairs_out, int32_t cow_cap,
+                         int32_t* n_cow_out);
+int pa_seq_append_batch_tokens(pa_pool* pool, const int32_t* seqs, int32_t count,
+                               const int32_t* n_tokens, const int32_t* tokens, int64_t* slots_out,
+                               int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out);
+int pa_block_state(const pa_pool* pool, int32_t block, int32_t* state_out);
+int pa_export_evictable(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
 
 /* ---------------------------------------------------------------- device ops
  * pa_reshape_and_cache: writes new tokens' K and V rows into their slots of layer

@@ -32,6 +32,26 @@ Where the pages are silent this model takes these readings:
   one reference.  Sequence ids are 0, 1, 2, ... and are never reused.
 * Free: references are dropped in logical order; each block that reaches zero is
   pushed onto the free stack.
+
+Automatic prefix caching ("vLLM explained", section on prefix caching): the cache
+lives in the same pool; a block is in use (reference count > 0), free and empty, or
+free but holding cached content; a request takes empty blocks first and only then
+evicts free cached blocks, least recently used first; blocks in use are never evicted.
+Readings where the pages are silent:
+
+* A full block's identity is the tuple of its sequence's token ids from the first
+  token through the block's last one (this model keys a dict on exactly that tuple).
+  Only full blocks are cached.
+* A block is registered when an append fills it, if every token of the sequence was
+  appended with its id and no block has that identity yet.  An append without ids
+  stops registration for the rest of the sequence's life (forks inherit this).
+* A new sequence with a prompt takes cached blocks (in use or free) for the prompt's
+  leading full blocks while their identities are cached, at most
+  ``(len(prompt) - 1) // block_size`` of them.
+* A block whose count reaches zero goes to the most-recent end of the LRU list if it
+  is cached, else onto the free stack.  With prefix caching on, free and release
+  drop references from the last logical block to the first.  Eviction forgets the
+  block's identity.
 """
 
 
@@ -53,6 +73,12 @@ class BlockManagerModel:
         self.tables = {}                        # live sequence id -> list of block ids
         self.lengths = {}                       # live sequence id -> token count
         self.next_id = 0
+        # prefix caching
+        self.caching = False
+        self.cache = {}                         # identity tuple -> cached block
+        self.identity = {}                      # cached block -> identity tuple
+        self.lru = []                           # free cached blocks, next evicted first
+        self.tokens = {}                        # live sequence -> token ids, or None
 
     # -- queries -----------------------------------------------------------------
     def free_stack_top_first(self):
@@ -60,7 +86,18 @@ class BlockManagerModel:
         return list(reversed(self.stack))
 
     def num_free(self):
-        return len(self.stack)
+        """Blocks an append may take: free and empty plus free and cached."""
+        return len(self.stack) + len(self.lru)
+
+    def evictable(self):
+        """Free cached blocks in the order they would be evicted."""
+        return list(self.lru)
+
+    def block_state(self, blk):
+        """0 free and empty, 1 in use, 2 free and cached."""
+        if self.refcount[blk] > 0:
+            return 1
+        return 2 if blk in self.identity else 0
 
     def table(self, seq):
         return list(self.tables[seq])
@@ -68,31 +105,81 @@ class BlockManagerModel:
     def length(self, seq):
         return self.lengths[seq]
 
+    # -- free lists --------------------------------------------------------------
+    def _pop(self):
+        if self.stack:
+            return self.stack.pop()
+        blk = self.lru.pop(0)
+        del self.cache[self.identity.pop(blk)]
+        return blk
+
+    def _release(self, blk):
+        self.refcount[blk] -= 1
+        if self.refcount[blk] == 0:
+            if blk in self.identity:
+                self.lru.append(blk)
+            else:
+                self.stack.append(blk)
+
     # -- operations --------------------------------------------------------------
+    def enable_prefix_caching(self):
+        if self.tables:
+            raise ValueError("sequences are live")
+        self.caching = True
+
     def seq_new(self):
         seq = self.next_id
         self.next_id += 1
         self.tables[seq] = []
         self.lengths[seq] = 0
+        self.tokens[seq] = []
         return seq
 
-    def seq_append(self, seq, n):
-        """Append ``n`` tokens; returns ``(slots, cow_pairs)``."""
+    def seq_new_prefix(self, prompt):
+        """New sequence sharing the cached blocks of the prompt's leading full blocks;
+        returns ``(seq, cached_tokens)``."""
+        if not self.caching:
+            raise ValueError("prefix caching is off")
+        prompt = [int(t) for t in prompt]
+        bs = self.block_size
+        seq = self.seq_new()
+        table = self.tables[seq]
+        limit = (len(prompt) - 1) // bs if prompt else 0
+        for j in range(limit):
+            blk = self.cache.get(tuple(prompt[:(j + 1) * bs]))
+            if blk is None:
+                break
+            if self.refcount[blk] == 0:
+                self.lru.remove(blk)
+            self.refcount[blk] += 1
+            table.append(blk)
+        n = len(table) * bs
+        self.lengths[seq] = n
+        self.tokens[seq] = prompt[:n]
+        return seq, n
+
+    def seq_append(self, seq, n, tokens=None):
+        """Append ``n`` tokens (ids in ``tokens``, or None); returns ``(slots, cow_pairs)``."""
         if seq not in self.tables:
             raise KeyError(seq)
         if n < 0:
             raise ValueError(n)
+        if tokens is not None and len(tokens) != n:
+            raise ValueError("one id per token")
         bs = self.block_size
         L = self.lengths[seq]
         table = self.tables[seq]
         needs_cow = n > 0 and L % bs != 0 and self.refcount[table[-1]] > 1
         fresh = sum(1 for pos in range(L, L + n) if pos % bs == 0)
-        if fresh + int(needs_cow) > len(self.stack):
+        if fresh + int(needs_cow) > self.num_free():
             raise OutOfBlocks()
+        if self.caching and tokens is None and n > 0:
+            self.tokens[seq] = None
+        known = self.tokens[seq] if self.caching else None
         cow_pairs = []
         if needs_cow:
             old = table[-1]
-            new = self.stack.pop()
+            new = self._pop()
             cow_pairs.append((old, new))
             self.refcount[old] -= 1
             self.refcount[new] = 1
@@ -100,10 +187,18 @@ class BlockManagerModel:
         slots = []
         for pos in range(L, L + n):
             if pos % bs == 0:
-                blk = self.stack.pop()
+                blk = self._pop()
                 self.refcount[blk] = 1
                 table.append(blk)
             slots.append(table[pos // bs] * bs + pos % bs)
+            if known is not None:
+                known.append(int(tokens[pos - L]))
+                if (pos + 1) % bs == 0:
+                    ident = tuple(known[:pos + 1])
+                    if ident not in self.cache:
+                        blk = table[pos // bs]
+                        self.cache[ident] = blk
+                        self.identity[blk] = ident
         self.lengths[seq] = L + n
         return slots, cow_pairs
 
@@ -113,6 +208,8 @@ class BlockManagerModel:
         child = self.seq_new()
         self.tables[child] = list(self.tables[parent])
         self.lengths[child] = self.lengths[parent]
+        known = self.tokens[parent]
+        self.tokens[child] = None if known is None else list(known)
         for blk in self.tables[child]:
             if blk >= 0:
                 self.refcount[blk] += 1
@@ -121,14 +218,13 @@ class BlockManagerModel:
     def seq_free(self, seq):
         if seq not in self.tables:
             raise KeyError(seq)
-        for blk in self.tables[seq]:
-            if blk < 0:
-                continue
-            self.refcount[blk] -= 1
-            if self.refcount[blk] == 0:
-                self.stack.append(blk)
+        row = self.tables[seq]
+        for blk in (reversed(row) if self.caching else row):
+            if blk >= 0:
+                self._release(blk)
         del self.tables[seq]
         del self.lengths[seq]
+        del self.tokens[seq]
 
     def seq_release_before(self, seq, token):
         """A sliding window has moved past ``token``: drop this sequence's hold on every
@@ -139,16 +235,13 @@ class BlockManagerModel:
         if seq not in self.tables or token < 0:
             raise KeyError(seq)
         table = self.tables[seq]
+        whole = [j for j in range(len(table) - 1) if (j + 1) * self.block_size <= token]
         dropped = 0
-        for j in range(len(table) - 1):
-            if (j + 1) * self.block_size > token:
-                break
+        for j in (reversed(whole) if self.caching else whole):
             blk = table[j]
             if blk < 0:
                 continue
-            self.refcount[blk] -= 1
-            if self.refcount[blk] == 0:
-                self.stack.append(blk)
+            self._release(blk)
             table[j] = -1
             dropped += 1
         return dropped
@@ -177,6 +270,13 @@ class BlockManagerModel:
         free = set(self.stack)
         assert len(free) == len(self.stack), "a block is on the free stack twice"
         assert all(self.refcount[b] == 0 for b in free)
-        assert len(free) + sum(1 for r in self.refcount if r > 0) == self.num_blocks
+        lru = set(self.lru)
+        assert len(lru) == len(self.lru), "a block is on the LRU list twice"
+        assert all(self.refcount[b] == 0 and b in self.identity for b in lru)
+        assert not (free & lru) and not any(b in self.identity for b in free)
+        assert len(free) + len(lru) + sum(1 for r in self.refcount if r > 0) == self.num_blocks
+        assert len(self.cache) == len(self.identity)
+        for ident, blk in self.cache.items():
+            assert self.identity[blk] == ident and len(ident) % self.block_size == 0 and ident
         for seq, row in self.tables.items():
             assert len(row) == -(-self.lengths[seq] // self.block_size)

@@ -71,6 +71,13 @@ _SIGNATURES = {
     "pa_decode_window": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _I32,
                                         ctypes.c_float, _I32, _P, _P, _I64, _P]),
     "pa_seq_release_before": (ctypes.c_int, [_P, _I32, _I32, _PI32]),
+    "pa_pool_enable_prefix_caching": (ctypes.c_int, [_P]),
+    "pa_seq_new_prefix": (ctypes.c_int, [_P, _PI32, _I32, _PI32, _PI32]),
+    "pa_seq_append_tokens": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI64, _PI32, _I32, _PI32]),
+    "pa_seq_append_batch_tokens": (ctypes.c_int, [_P, _PI32, _I32, _PI32, _PI32, _PI64, _PI32, _I32,
+                                                  _PI32]),
+    "pa_block_state": (ctypes.c_int, [_P, _I32, _PI32]),
+    "pa_export_evictable": (ctypes.c_int, [_P, _PI32, _I32, _PI32]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 
@@ -228,6 +235,70 @@ def pa_seq_append_batch(pool, seqs, n_tokens=None):
                                      slots.ctypes.data_as(_PI64), _i32p(pairs), cap,
                                      ctypes.byref(n_cow)))
     return slots[:total], [(int(pairs[2 * i]), int(pairs[2 * i + 1])) for i in range(n_cow.value)]
+
+
+def pa_seq_append_tokens(pool, seq, tokens):
+    """``pa_seq_append`` with the tokens' ids; returns ``(slots, cow_pairs)``."""
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    n = len(tokens)
+    slots = np.zeros(max(1, n), dtype=np.int64)
+    pairs = np.zeros(2, dtype=np.int32)
+    n_cow = ctypes.c_int32()
+    _check(lib().pa_seq_append_tokens(pool.handle, seq, _i32p(tokens), n, slots.ctypes.data_as(_PI64),
+                                      _i32p(pairs), 1, ctypes.byref(n_cow)))
+    return slots[:n], [(int(pairs[0]), int(pairs[1]))] if n_cow.value else []
+
+
+def pa_seq_append_batch_tokens(pool, seqs, tokens, n_tokens=None):
+    """``pa_seq_append_batch`` with the ids of every appended token, back to back."""
+    seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+    counts = np.ones(len(seqs), np.int32) if n_tokens is None else \
+        np.ascontiguousarray(n_tokens, dtype=np.int32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    total = int(counts.sum())
+    if len(tokens) != total:
+        raise ValueError("one token id per appended token")
+    slots = np.zeros(max(1, total), dtype=np.int64)
+    tok = tokens if total else np.zeros(1, np.int32)
+    cap = max(1, len(seqs))
+    pairs = np.zeros(2 * cap, dtype=np.int32)
+    n_cow = ctypes.c_int32()
+    _check(lib().pa_seq_append_batch_tokens(pool.handle, _i32p(seqs), len(seqs),
+                                            None if n_tokens is None else _i32p(counts), _i32p(tok),
+                                            slots.ctypes.data_as(_PI64), _i32p(pairs), cap,
+                                            ctypes.byref(n_cow)))
+    return slots[:total], [(int(pairs[2 * i]), int(pairs[2 * i + 1])) for i in range(n_cow.value)]
+
+
+def pa_pool_enable_prefix_caching(pool):
+    _check(lib().pa_pool_enable_prefix_caching(pool.handle))
+
+
+def pa_seq_new_prefix(pool, prompt):
+    """Returns ``(seq, n_cached_tokens)``."""
+    prompt = np.ascontiguousarray(prompt, dtype=np.int32)
+    buf = prompt if len(prompt) else np.zeros(1, np.int32)
+    s, c = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pa_seq_new_prefix(pool.handle, _i32p(buf), len(prompt), ctypes.byref(s),
+                                   ctypes.byref(c)))
+    return s.value, c.value
+
+
+BLOCK_FREE_EMPTY, BLOCK_IN_USE, BLOCK_FREE_CACHED = 0, 1, 2
+
+
+def pa_block_state(pool, block):
+    st = ctypes.c_int32()
+    _check(lib().pa_block_state(pool.handle, block, ctypes.byref(st)))
+    return st.value
+
+
+def pa_export_evictable(pool):
+    cap = pool.num_blocks
+    out = np.zeros(max(1, cap), dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(lib().pa_export_evictable(pool.handle, _i32p(out), cap, ctypes.byref(n)))
+    return out[:n.value]
 
 
 def pa_seq_fork(pool, parent):

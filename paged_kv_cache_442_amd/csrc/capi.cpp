@@ -276,34 +276,84 @@ int pa_seq_new(pa_pool* pool, int32_t* seq_out) {
   return mgr_status(pool->mgr->seq_new(seq_out), "pa_seq_new");
 }
 
-int pa_seq_append(pa_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots_out,
-                  int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out) {
-  if (!pool || !n_cow_out) return fail(PA_E_INVAL, "pool and n_cow_out must be non-NULL");
-  if (n_tokens > 0 && !slots_out) return fail(PA_E_INVAL, "slots_out is NULL");
-  if (cow_cap < 0 || (cow_cap > 0 && !cow_pairs_out)) return fail(PA_E_INVAL, "bad cow_pairs_out / cow_cap");
+static int append_one(pa_pool* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens,
+               int64_t* slots_out, int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out,
+               const char* what) {
+  if (!pool || !n_cow_out) return fail(PA_E_INVAL, "%s: pool and n_cow_out must be non-NULL", what);
+  if (n_tokens > 0 && !slots_out) return fail(PA_E_INVAL, "%s: slots_out is NULL", what);
+  if (cow_cap < 0 || (cow_cap > 0 && !cow_pairs_out))
+    return fail(PA_E_INVAL, "%s: bad cow_pairs_out / cow_cap", what);
   int32_t dummy_pair[2];
   int32_t* pairs = cow_cap > 0 ? cow_pairs_out : dummy_pair;
   int32_t n_cow = 0;
-  int st = mgr_status(pool->mgr->seq_append(seq, n_tokens, slots_out, pairs, cow_cap, &n_cow),
-                      "pa_seq_append");
+  int st = mgr_status(pool->mgr->seq_append(seq, n_tokens, tokens, slots_out, pairs, cow_cap, &n_cow),
+                      what);
   if (st == PA_OK) *n_cow_out = n_cow;
   return st;
+}
+
+static int append_batch(pa_pool* pool, const int32_t* seqs, int32_t count, const int32_t* n_tokens,
+                 const int32_t* tokens, int64_t* slots_out, int32_t* cow_pairs_out, int32_t cow_cap,
+                 int32_t* n_cow_out, const char* what) {
+  if (!pool || !n_cow_out) return fail(PA_E_INVAL, "%s: pool and n_cow_out must be non-NULL", what);
+  if (count < 0 || (count > 0 && (!seqs || !slots_out)))
+    return fail(PA_E_INVAL, "%s: bad seqs / count / slots_out", what);
+  if (cow_cap < 0 || (cow_cap > 0 && !cow_pairs_out))
+    return fail(PA_E_INVAL, "%s: bad cow_pairs_out / cow_cap", what);
+  int32_t dummy_pair[2];
+  int32_t* pairs = cow_cap > 0 ? cow_pairs_out : dummy_pair;
+  int32_t n_cow = 0;
+  int st = mgr_status(pool->mgr->seq_append_batch(seqs, count, n_tokens, tokens, slots_out, pairs,
+                                                  cow_cap, &n_cow),
+                      what);
+  if (st == PA_OK) *n_cow_out = n_cow;
+  return st;
+}
+
+int pa_seq_append(pa_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                  int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out) {
+  return append_one(pool, seq, nullptr, n_tokens, slots_out, cow_pairs_out, cow_cap, n_cow_out,
+                    "pa_seq_append");
+}
+
+int pa_seq_append_tokens(pa_pool* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens,
+                         int64_t* slots_out, int32_t* cow_pairs_out, int32_t cow_cap,
+                         int32_t* n_cow_out) {
+  if (n_tokens > 0 && !tokens) return fail(PA_E_INVAL, "pa_seq_append_tokens: tokens is NULL");
+  return append_one(pool, seq, tokens, n_tokens, slots_out, cow_pairs_out, cow_cap, n_cow_out,
+                    "pa_seq_append_tokens");
 }
 
 int pa_seq_append_batch(pa_pool* pool, const int32_t* seqs, int32_t count, const int32_t* n_tokens,
                         int64_t* slots_out, int32_t* cow_pairs_out, int32_t cow_cap,
                         int32_t* n_cow_out) {
-  if (!pool || !n_cow_out) return fail(PA_E_INVAL, "pool and n_cow_out must be non-NULL");
-  if (count < 0 || (count > 0 && (!seqs || !slots_out)))
-    return fail(PA_E_INVAL, "bad seqs / count / slots_out");
-  if (cow_cap < 0 || (cow_cap > 0 && !cow_pairs_out)) return fail(PA_E_INVAL, "bad cow_pairs_out / cow_cap");
-  int32_t dummy_pair[2];
-  int32_t* pairs = cow_cap > 0 ? cow_pairs_out : dummy_pair;
-  int32_t n_cow = 0;
-  int st = mgr_status(pool->mgr->seq_append_batch(seqs, count, n_tokens, slots_out, pairs, cow_cap, &n_cow),
-                      "pa_seq_append_batch");
-  if (st == PA_OK) *n_cow_out = n_cow;
-  return st;
+  return append_batch(pool, seqs, count, n_tokens, nullptr, slots_out, cow_pairs_out, cow_cap,
+                      n_cow_out, "pa_seq_append_batch");
+}
+
+int pa_seq_append_batch_tokens(pa_pool* pool, const int32_t* seqs, int32_t count,
+                               const int32_t* n_tokens, const int32_t* tokens, int64_t* slots_out,
+                               int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out) {
+  if (count > 0 && !tokens) return fail(PA_E_INVAL, "pa_seq_append_batch_tokens: tokens is NULL");
+  return append_batch(pool, seqs, count, n_tokens, tokens, slots_out, cow_pairs_out, cow_cap,
+                      n_cow_out, "pa_seq_append_batch_tokens");
+}
+
+int pa_pool_enable_prefix_caching(pa_pool* pool) {
+  if (!pool) return fail(PA_E_INVAL, "pool is NULL");
+  if (pool->mgr->enable_prefix_caching() != pa::MgrStatus::ok)
+    return fail(PA_E_INVAL, "pa_pool_enable_prefix_caching: sequences are live");
+  return ok();
+}
+
+int pa_seq_new_prefix(pa_pool* pool, const int32_t* prompt, int32_t n_prompt, int32_t* seq_out,
+                      int32_t* n_cached_out) {
+  if (!pool || !seq_out || !n_cached_out)
+    return fail(PA_E_INVAL, "pool, seq_out and n_cached_out must be non-NULL");
+  if (!pool->mgr->prefix_caching()) return fail(PA_E_INVAL, "pa_seq_new_prefix: prefix caching is off");
+  if (n_prompt < 0 || (n_prompt > 0 && !prompt)) return fail(PA_E_INVAL, "pa_seq_new_prefix: bad prompt");
+  return mgr_status(pool->mgr->seq_new_prefix(prompt, n_prompt, seq_out, n_cached_out),
+                    "pa_seq_new_prefix");
 }
 
 int pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* child_out) {
@@ -353,6 +403,23 @@ int pa_block_refcount(const pa_pool* pool, int32_t block, int32_t* rc_out) {
 int pa_num_free_blocks(const pa_pool* pool, int32_t* n_out) {
   if (!pool || !n_out) return fail(PA_E_INVAL, "pool and n_out must be non-NULL");
   *n_out = pool->mgr->num_free();
+  return ok();
+}
+
+int pa_block_state(const pa_pool* pool, int32_t block, int32_t* state_out) {
+  if (!pool || !state_out) return fail(PA_E_INVAL, "pool and state_out must be non-NULL");
+  if (block < 0 || block >= pool->desc.num_blocks) return fail(PA_E_INVAL, "block %d out of range", block);
+  *state_out = static_cast<int32_t>(pool->mgr->state(block));
+  return ok();
+}
+
+int pa_export_evictable(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out) {
+  if (!pool || !n_out || cap < 0 || (cap > 0 && !out)) return fail(PA_E_INVAL, "bad arguments");
+  std::vector<int32_t> v;
+  pool->mgr->evictable_lru_first(&v);
+  *n_out = static_cast<int32_t>(v.size());
+  if (static_cast<int64_t>(v.size()) > cap) return fail(PA_E_RANGE, "cap %d < %zu evictable blocks", cap, v.size());
+  for (size_t i = 0; i < v.size(); ++i) out[i] = v[i];
   return ok();
 }
 

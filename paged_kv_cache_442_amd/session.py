@@ -9,6 +9,7 @@ here is argument marshalling and call order; every computation runs in libpa.
 """
 
 import math
+import time
 
 import numpy as np
 import torch
@@ -255,3 +256,87 @@ class PrefillSession:
         self.prefill(stream)
         self.decode(stream)
 
+
+
+class PrefixCacheSession:
+    """Serve a ``workloads.PrefixCacheWorkload`` on a pool with prefix caching.
+
+    Requests are admitted one after another.  Admitting request ``i`` frees request
+    ``i - release_after - 1`` (its full blocks stay cached until evicted), looks the
+    prompt up (``pa_seq_new_prefix``), appends the rest of the prompt and the decode
+    tokens with their ids, and writes K/V rows for those tokens only: the cached
+    blocks already hold the rest.  ``decode`` then runs ``pa_decode`` over any set of
+    live requests.
+    """
+
+    def __init__(self, w, device="cuda", poison=True):
+        self.w = w
+        self.device = device
+        self.desc = pa.make_desc(1, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype)
+        self.storage = torch.empty(pa.pa_pool_bytes(self.desc), dtype=torch.uint8, device=device)
+        if poison:
+            nan_fill(self.storage, w.dtype)
+        self.pool = pa.pa_alloc_pool(self.desc, self.storage, w.free_order)
+        pa.pa_pool_enable_prefix_caching(self.pool)
+        self.scale = 1.0 / math.sqrt(w.head_dim)
+        self.seq_of = {}
+        R = w.num_requests
+        self.cached_tokens = np.zeros(R, dtype=np.int64)
+        self.evicted = np.zeros(R, dtype=np.int64)   # cached blocks evicted to admit request i
+        self.host_seconds = np.zeros(R)              # manager calls of each admission
+
+    def admit(self, i, stream=None):
+        w = self.w
+        gone = i - w.release_after - 1
+        if gone >= 0 and gone in self.seq_of:
+            pa.pa_seq_free(self.pool, self.seq_of.pop(gone))
+        toks = w.tokens(i)
+        prompt = w.prompt(i)
+        empty = len(pa.pa_export_free_stack(self.pool))
+        t0 = time.perf_counter()
+        seq, hit = pa.pa_seq_new_prefix(self.pool, prompt)
+        slots, cow = pa.pa_seq_append_tokens(self.pool, seq, toks[hit:])
+        self.host_seconds[i] = time.perf_counter() - t0
+        new_blocks = -(-len(toks) // w.block_size) - hit // w.block_size
+        self.evicted[i] = max(0, new_blocks - empty)
+        if cow:
+            raise RuntimeError("no sequence is shared by forking here")
+        self.seq_of[i] = seq
+        self.cached_tokens[i] = hit
+        k, v = w.kv_rows(toks[hit:], np.arange(hit, len(toks)))
+        pa.pa_reshape_and_cache(self.pool, 0, bits_to_device(k, w.dtype, self.device),
+                                bits_to_device(v, w.dtype, self.device),
+                                torch.from_numpy(np.ascontiguousarray(slots)).to(self.device), stream)
+
+    def live(self):
+        return sorted(self.seq_of)
+
+    def decode_args(self, requests):
+        """Device-resident decode arguments for ``requests`` (tables exported now)."""
+        w = self.w
+        seqs = [self.seq_of[r] for r in requests]
+        lens = [len(w.tokens(r)) for r in requests]
+        max_blocks = max(1, max(-(-L // w.block_size) for L in lens))
+        tables, ctx = pa.pa_export_block_tables(self.pool, seqs, max_blocks)
+        dev = self.device
+        return {
+            "q": bits_to_device(w.q[list(requests)], w.dtype, dev),
+            "tables": torch.from_numpy(tables).to(dev),
+            "ctx": torch.from_numpy(ctx).to(dev),
+            "max_context": max(lens),
+            "out": torch.empty(len(requests), w.num_q_heads, w.head_dim, dtype=torch.float32,
+                               device=dev),
+            "ws": torch.empty(pa.pa_decode_workspace_bytes(self.pool, len(requests), w.num_q_heads,
+                                                           max(lens), 0),
+                              dtype=torch.uint8, device=dev),
+            "tables_host": tables,
+        }
+
+    def run_decode(self, a, stream=None):
+        pa.pa_decode(self.pool, 0, a["q"], a["tables"], a["ctx"], a["max_context"], self.scale,
+                     a["out"], a["ws"], 0, stream)
+        return a["out"]
+
+    def decode(self, requests, stream=None):
+        """Decode the newest token of each request in ``requests``; returns ``out``."""
+        return self.run_decode(self.decode_args(requests), stream)

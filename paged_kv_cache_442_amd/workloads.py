@@ -21,6 +21,9 @@ shapes; no weights are involved):
 * ``chunked_prefill`` -- 8 prefill chunks of 256..512 query tokens over cached
                   prefixes of 0..4096 tokens plus 96 decode rows of length 1..4096;
                   GQA 32/8, bf16, block size 32.
+* ``prefix_cache`` -- requests that share system prompts (prefix caching): each
+                  prompt is one of a few system prompts followed by the request's own
+                  tokens; a token's K/V rows depend only on its id and position.
 
 Values are float32 draws from N(0, 1) (numpy PCG64, ``default_rng(seed)``) rounded
 to the storage format with round-to-nearest-even; arrays hold raw bits (uint16
@@ -285,3 +288,85 @@ def custom_chunked(seed, dtype, prefix_lens, chunk_lens, decode_lens, num_q_head
                                   prefix_lens, chunk_lens, decode_lens, perm, q_chunks, q_decode,
                                   k, v)
 
+
+
+@dataclass
+class PrefixCacheWorkload:
+    """Requests sharing system prompts, served one after another by a prefix-caching pool.
+
+    Request ``i`` has prompt ``system[sys_of[i]] + user[i]`` and then decodes ``steps``
+    tokens ``decode_tokens[i]``.  Token ids are drawn from ``[0, vocab)``.  K and V rows of
+    a token are ``(tok[id] + pos[position]) / sqrt(2)`` from two seeded tables each,
+    rounded to the storage format: equal prefixes always give equal rows, which is what
+    a cache hit relies on (in a model the rows depend on the whole prefix; a function
+    of (id, position) is the simplest stand-in with that property).
+    """
+    dtype: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    vocab: int
+    system: list
+    sys_of: np.ndarray
+    user: list
+    decode_tokens: np.ndarray
+    release_after: int
+    free_order: np.ndarray
+    q: np.ndarray
+    tok_k: np.ndarray
+    tok_v: np.ndarray
+    pos_k: np.ndarray
+    pos_v: np.ndarray
+
+    @property
+    def num_requests(self):
+        return len(self.user)
+
+    def prompt(self, i):
+        return np.concatenate([self.system[int(self.sys_of[i])], self.user[i]]).astype(np.int32)
+
+    def tokens(self, i):
+        """Every token of request ``i`` after its decode steps."""
+        return np.concatenate([self.prompt(i), self.decode_tokens[i]]).astype(np.int32)
+
+    def kv_rows(self, token_ids, positions):
+        """Raw bits of the K and V rows ``[n][H_kv][d]`` of tokens at positions."""
+        t = np.asarray(token_ids, dtype=np.int64)
+        p = np.asarray(positions, dtype=np.int64) % self.pos_k.shape[0]
+        c = np.float32(1.0 / math.sqrt(2.0))
+        k = (self.tok_k[t] + self.pos_k[p]) * c
+        v = (self.tok_v[t] + self.pos_v[p]) * c
+        return round_to_bits(k, self.dtype), round_to_bits(v, self.dtype)
+
+
+def prefix_cache(seed=6, num_requests=48, num_system=4, min_system=100, max_system=700,
+                 min_user=1, max_user=200, steps=1, vocab=512, num_q_heads=32, num_kv_heads=8,
+                 head_dim=128, block_size=16, pool_fraction=0.5, release_after=4, dtype=BF16,
+                 num_positions=4096):
+    """Prefix-cache workload.  The pool holds ``pool_fraction`` of the blocks the requests
+    would take without sharing (so cached blocks are evicted); a request is freed
+    ``release_after`` requests after it starts."""
+    rng = np.random.default_rng(seed)
+    sys_lens = rng.integers(min_system, max_system + 1, size=num_system)
+    system = [rng.integers(0, vocab, size=int(n)).astype(np.int32) for n in sys_lens]
+    sys_of = rng.integers(0, num_system, size=num_requests)
+    user_lens = rng.integers(min_user, max_user + 1, size=num_requests)
+    user = [rng.integers(0, vocab, size=int(n)).astype(np.int32) for n in user_lens]
+    decode_tokens = rng.integers(0, vocab, size=(num_requests, steps)).astype(np.int32)
+    total = sum(_blocks(len(system[int(sys_of[i])]) + len(user[i]) + steps, block_size)
+                for i in range(num_requests))
+    live_peak = max(sum(_blocks(len(system[int(sys_of[j])]) + len(user[j]) + steps, block_size)
+                        for j in range(i, min(i + release_after + 1, num_requests)))
+                    for i in range(num_requests))
+    N = max(live_peak + 2, int(math.ceil(pool_fraction * total)))
+    perm = rng.permutation(N).astype(np.int32)
+    q = _normal_bits(rng, (num_requests, num_q_heads, head_dim), dtype)
+    tok_k = rng.standard_normal((vocab, num_kv_heads, head_dim), dtype=np.float32)
+    tok_v = rng.standard_normal((vocab, num_kv_heads, head_dim), dtype=np.float32)
+    pos_k = rng.standard_normal((num_positions, num_kv_heads, head_dim), dtype=np.float32)
+    pos_v = rng.standard_normal((num_positions, num_kv_heads, head_dim), dtype=np.float32)
+    return PrefixCacheWorkload(dtype, num_q_heads, num_kv_heads, head_dim, block_size, N, vocab,
+                               system, sys_of, user, decode_tokens, release_after, perm, q,
+                               tok_k, tok_v, pos_k, pos_v)
