@@ -33,6 +33,8 @@ WORKLOADS = {
     "mixed_chunked": "Mixed batch, one layer: 8 prefill chunks of 256-512 causal query rows over "
                      "cached prefixes of 0-4096 tokens plus 96 decode rows of 1-4096 tokens; GQA "
                      "32/8, d 128, bf16, block 32",
+    "swap": "Swap preemption, one Llama-3-70B-shaped layer (the llama3_70b cache): every 4th of "
+            "the 128 sequences swapped out to pinned host memory and back in",
     "prefix_cache": "Prefix caching, one layer: 256 requests served in order over 8 system prompts "
                     "of 512-4096 tokens plus 16-256 own tokens, 128 live at a time, GQA 64/8, d 128, "
                     "bf16, block 16; decode of the 128 live requests over shared cached blocks",
@@ -188,6 +190,8 @@ def main():
         return bench_mixed(args, torch)
     if args.workload == "prefix_cache":
         return bench_prefix_cache(args, torch)
+    if args.workload == "swap":
+        return bench_swap(args, torch)
 
     t0 = time.perf_counter()
     w = make_workload(args.workload, args.num_q_heads, args.fixed_len)
@@ -462,6 +466,109 @@ def bench_mixed(args, torch):
         },
         "decode_rows_GBps": round(decode_bytes / (decode_ms * 1e-3) / 1e9, 2),
         "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_swap(args, torch):
+    """Swap preemption: pa_seq_swap_out / pa_seq_swap_in on the host, pa_swap_blocks
+    (one launch moving whole blocks over the host link) timed each way; a torch copy of
+    the same byte count between pinned host memory and the device is the measured
+    ceiling of the link."""
+    from paged_kv_cache_442_amd import binding as pa
+    from paged_kv_cache_442_amd import workloads as wl
+    from paged_kv_cache_442_amd.session import DecodeSession
+    from oracle import attention, fpbits
+
+    w = wl.llama3_70b()
+    sess = DecodeSession(w)
+    sess.write_new_tokens()          # every token of every sequence is in the cache
+    torch.cuda.synchronize()
+    pool = sess.pool
+    victims = list(range(0, w.num_seqs, 4))
+    vseqs = [sess.seqs[i] for i in victims]
+    tables, _ = pa.pa_export_block_tables(pool, vseqs, sess.max_blocks)
+    n_blocks = int((tables >= 0).sum())
+    M = n_blocks
+    pa.pa_pool_set_swap_space(pool, M)
+    host = torch.empty(pa.pa_swap_space_bytes(sess.desc, M), dtype=torch.uint8, pin_memory=True)
+    block_bytes = pa.pa_block_bytes(sess.desc)
+    nbytes = n_blocks * block_bytes
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    out_ms, in_ms = [], []
+    for it in range(args.warmup + max(1, args.steps // 10)):
+        t0 = time.perf_counter()
+        pairs = pa.pa_seq_swap_out(pool, vseqs)
+        host_out_us = (time.perf_counter() - t0) * 1e6
+        p_out = torch.tensor(pairs, dtype=torch.int32).reshape(-1, 2).cuda()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        pa.pa_swap_blocks(pool, host, p_out, True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        pairs_in = pa.pa_seq_swap_in(pool, vseqs)
+        host_in_us = (time.perf_counter() - t0) * 1e6
+        p_in = torch.tensor(pairs_in, dtype=torch.int32).reshape(-1, 2).cuda()
+        e2, e3 = ev(), ev()
+        e2.record(stream)
+        pa.pa_swap_blocks(pool, host, p_in, False)
+        e3.record(stream)
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            out_ms.append(e0.elapsed_time(e1))
+            in_ms.append(e2.elapsed_time(e3))
+    # The swapped sequences decode correctly from their new blocks.
+    tables, ctx = pa.pa_export_block_tables(pool, sess.seqs, sess.max_blocks)
+    sess.tables.copy_(torch.from_numpy(tables))
+    sess.decode()
+    torch.cuda.synchronize()
+    got = sess.out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for s_ in victims[:2]:
+        kt, vt = w.seq_tokens(s_)
+        want = attention.contiguous_decode(w.dtype, w.q[s_], fpbits.decode(w.dtype, kt),
+                                           fpbits.decode(w.dtype, vt), attention.default_scale(w.head_dim))
+        worst = max(worst, float(np.max(np.abs(got[s_] - want))))
+    # Ceiling: one contiguous DMA copy of the same size each way.
+    dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    hview = host[:nbytes]
+    ceil = {}
+    for name, fn in (("d2h", lambda: hview.copy_(dev, non_blocking=True)),
+                     ("h2d", lambda: dev.copy_(hview, non_blocking=True))):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(3):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ceil[name] = nbytes / (e0.elapsed_time(e1) / 3 * 1e-3) / 1e9
+    out_gbps = nbytes / (float(np.mean(out_ms)) * 1e-3) / 1e9
+    in_gbps = nbytes / (float(np.mean(in_ms)) * 1e-3) / 1e9
+    line = {
+        "metric": "paged-decode KV GB/s and % of HBM peak at 1 MI355X; tokens/sec per layer",
+        "value": round(min(out_gbps, in_gbps), 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": len(out_ms), "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean(out_ms)) + float(np.mean(in_ms)), 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/Q, seeded block permutation)",
+        "config": {"workload": "swap", "description": WORKLOADS["swap"],
+                   "swapped_sequences": len(victims), "blocks_moved": n_blocks,
+                   "bytes_each_way": nbytes},
+        "swap_out_GBps": round(out_gbps, 2), "swap_in_GBps": round(in_gbps, 2),
+        "swap_out_ms": round(float(np.mean(out_ms)), 4), "swap_in_ms": round(float(np.mean(in_ms)), 4),
+        "host_manager_us": {"swap_out": round(host_out_us, 1), "swap_in": round(host_in_us, 1)},
+        "roofline": {"bound": "host link", "kernel": "swap_blocks_kernel",
+                     "achieved": round(min(out_gbps, in_gbps), 2),
+                     "peak": round(min(ceil["d2h"], ceil["h2d"]), 2), "unit": "GB/s",
+                     "frac": round(min(out_gbps / ceil["d2h"], in_gbps / ceil["h2d"]), 4),
+                     "traffic": None,
+                     "note": "peak = measured contiguous DMA copy of the same size (torch), each way"},
+        "dma_ceiling_GBps": {k: round(v, 2) for k, v in ceil.items()},
+        "max_abs_err_sampled": worst, "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

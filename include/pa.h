@@ -214,6 +214,56 @@ int pa_seq_append_batch_tokens(pa_pool* pool, const int32_t* seqs, int32_t count
 int pa_block_state(const pa_pool* pool, int32_t block, int32_t* state_out);
 int pa_export_evictable(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
 
+/* ---------------------------------------------------------------- swap preemption
+ * When blocks run short, a request can be preempted and its KV moved to CPU memory
+ * (swap) instead of being recomputed later ("vLLM explained", jackchen890311.github.io,
+ * table on when KV may be overwritten).
+ *
+ * The swap space is caller-owned pinned host memory laid out like the pool, with its
+ * own block count M: [num_layers][K|V][M][num_kv_heads][block_size][head_dim]
+ * (pa_swap_space_bytes).  The manager keeps a LIFO free stack of host blocks (0 first)
+ * and their reference counts.
+ *
+ * Rules where the pages are silent (deterministic, all-or-nothing):
+ *   - pa_seq_swap_out(seqs): every distinct device block in the tables of the given
+ *     sequences (distinct, live, resident) gets one host block, in order of first use
+ *     (sequence order, then logical order); a block shared by several of them is
+ *     copied once.  The pairs (device, host) are reported; the tables now name host
+ *     blocks; each sequence then drops its device references as pa_seq_free would
+ *     (blocks reaching zero go back to the free stack, or the LRU list if cached).
+ *     PA_E_NOMEM if the swap space is short, PA_E_RANGE if cap is short.
+ *   - pa_seq_swap_in(seqs): the mirror image: each distinct host block gets a device
+ *     block (taken as an append takes them: empty first, then eviction), pairs (host,
+ *     device) reported; host references dropped in logical order.
+ *   - A swapped-out sequence may only be swapped in or freed: appends, forks, window
+ *     releases and table exports are PA_E_INVAL.  Swapped-in blocks are not entered
+ *     into the prefix cache.
+ *   - The caller copies the reported pairs with pa_swap_blocks, on the stream that
+ *     later reuses the freed blocks, before that reuse (swap-out) or before the next
+ *     decode of the sequences (swap-in).
+ *
+ * pa_swap_space_bytes: bytes of a swap space of host_blocks blocks for this layout.
+ * pa_pool_set_swap_space: sizes the manager's swap space (PA_E_INVAL while a sequence
+ *   is swapped out).
+ * pa_swap_blocks: copies whole blocks (every layer, K and V) for n_pairs pairs (device
+ *   int32 [n_pairs][2]): to_host != 0 copies device block -> host block (swap-out
+ *   pairs), to_host == 0 host block -> device block (swap-in pairs).  host_base: pinned
+ *   host memory (hipHostMalloc, or a pinned torch tensor) of at least
+ *   pa_swap_space_bytes bytes, 16-byte aligned; the kernel reads or writes it through
+ *   its device mapping, so memory without one is PA_E_INVAL.  Pairs naming a block
+ *   outside either side are skipped.  Asynchronous on `stream`. */
+int64_t pa_swap_space_bytes(const pa_pool_desc* desc, int32_t host_blocks);
+int pa_pool_set_swap_space(pa_pool* pool, int32_t host_blocks);
+int pa_seq_swap_out(pa_pool* pool, const int32_t* seqs, int32_t count, int32_t* pairs_out,
+                    int32_t cap, int32_t* n_pairs_out);
+int pa_seq_swap_in(pa_pool* pool, const int32_t* seqs, int32_t count, int32_t* pairs_out,
+                   int32_t cap, int32_t* n_pairs_out);
+int pa_seq_swapped(const pa_pool* pool, int32_t seq, int32_t* swapped_out);
+int pa_host_block_refcount(const pa_pool* pool, int32_t host_block, int32_t* rc_out);
+int pa_export_host_free_stack(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
+int pa_swap_blocks(pa_pool* pool, void* host_base, int64_t host_bytes, const int32_t* pairs,
+                   int32_t n_pairs, int32_t to_host, void* stream);
+
 /* ---------------------------------------------------------------- device ops
  * pa_reshape_and_cache: writes new tokens' K and V rows into their slots of layer
  *   `layer` (a bit copy).  k, v: device [n_tokens][num_kv_heads][head_dim] in the

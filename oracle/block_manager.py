@@ -52,6 +52,17 @@ Readings where the pages are silent:
   is cached, else onto the free stack.  With prefix caching on, free and release
   drop references from the last logical block to the first.  Eviction forgets the
   block's identity.
+
+Swap preemption ("vLLM explained", table on when KV may be overwritten: a preempted
+request's KV is recomputed later or moved to CPU memory).  Readings:
+
+* A swap space of host blocks, LIFO free stack (0 first), its own reference counts.
+* Swapping out a list of sequences gives each distinct device block in their tables
+  one host block, in order of first use (sequence order, then logical order), and
+  reports (device, host) pairs; tables then name host blocks, and each sequence drops
+  its device references as a free would.  Swapping in is the mirror image, taking
+  device blocks as an append does; host references are dropped in logical order.
+  Both are all-or-nothing.  A swapped-out sequence may only be swapped in or freed.
 """
 
 
@@ -79,6 +90,10 @@ class BlockManagerModel:
         self.identity = {}                      # cached block -> identity tuple
         self.lru = []                           # free cached blocks, next evicted first
         self.tokens = {}                        # live sequence -> token ids, or None
+        # swap preemption
+        self.host_stack = []                    # top of stack = end of the list
+        self.host_refcount = []
+        self.swapped = set()
 
     # -- queries -----------------------------------------------------------------
     def free_stack_top_first(self):
@@ -135,6 +150,81 @@ class BlockManagerModel:
         self.tokens[seq] = []
         return seq
 
+    def set_swap_space(self, host_blocks):
+        if self.swapped:
+            raise ValueError("sequences are swapped out")
+        self.host_refcount = [0] * host_blocks
+        self.host_stack = list(reversed(range(host_blocks)))
+
+    def host_free_stack_top_first(self):
+        return list(reversed(self.host_stack))
+
+    def _check_resident(self, seq):
+        if seq not in self.tables:
+            raise KeyError(seq)
+        if seq in self.swapped:
+            raise ValueError("sequence %d is swapped out" % seq)
+
+    def _release_all(self, row):
+        for blk in (reversed(row) if self.caching else row):
+            if blk >= 0:
+                self._release(blk)
+
+    def seq_swap_out(self, seqs):
+        """Move ``seqs`` to host blocks; returns the (device, host) pairs to copy."""
+        for i, seq in enumerate(seqs):
+            self._check_resident(seq)
+            if seq in seqs[:i]:
+                raise ValueError("a sequence is listed twice")
+        distinct = {b for seq in seqs for b in self.tables[seq] if b >= 0}
+        if len(distinct) > len(self.host_stack):
+            raise OutOfBlocks()
+        to_host, pairs = {}, []
+        for seq in seqs:
+            row = self.tables[seq]
+            device = list(row)
+            for j, blk in enumerate(row):
+                if blk < 0:
+                    continue
+                if blk not in to_host:
+                    to_host[blk] = self.host_stack.pop()
+                    pairs.append((blk, to_host[blk]))
+                self.host_refcount[to_host[blk]] += 1
+                row[j] = to_host[blk]
+            self._release_all(device)
+            self.swapped.add(seq)
+        return pairs
+
+    def seq_swap_in(self, seqs):
+        """Move swapped-out ``seqs`` back to device blocks; returns (host, device) pairs."""
+        for i, seq in enumerate(seqs):
+            if seq not in self.tables or seq not in self.swapped:
+                raise ValueError("sequence %d is not swapped out" % seq)
+            if seq in seqs[:i]:
+                raise ValueError("a sequence is listed twice")
+        distinct = {h for seq in seqs for h in self.tables[seq] if h >= 0}
+        if len(distinct) > self.num_free():
+            raise OutOfBlocks()
+        to_dev, pairs = {}, []
+        for seq in seqs:
+            row = self.tables[seq]
+            host = list(row)
+            for j, h in enumerate(row):
+                if h < 0:
+                    continue
+                if h not in to_dev:
+                    to_dev[h] = self._pop()
+                    pairs.append((h, to_dev[h]))
+                self.refcount[to_dev[h]] += 1
+                row[j] = to_dev[h]
+            for h in host:
+                if h >= 0:
+                    self.host_refcount[h] -= 1
+                    if self.host_refcount[h] == 0:
+                        self.host_stack.append(h)
+            self.swapped.discard(seq)
+        return pairs
+
     def seq_new_prefix(self, prompt):
         """New sequence sharing the cached blocks of the prompt's leading full blocks;
         returns ``(seq, cached_tokens)``."""
@@ -160,8 +250,7 @@ class BlockManagerModel:
 
     def seq_append(self, seq, n, tokens=None):
         """Append ``n`` tokens (ids in ``tokens``, or None); returns ``(slots, cow_pairs)``."""
-        if seq not in self.tables:
-            raise KeyError(seq)
+        self._check_resident(seq)
         if n < 0:
             raise ValueError(n)
         if tokens is not None and len(tokens) != n:
@@ -203,8 +292,7 @@ class BlockManagerModel:
         return slots, cow_pairs
 
     def seq_fork(self, parent):
-        if parent not in self.tables:
-            raise KeyError(parent)
+        self._check_resident(parent)
         child = self.seq_new()
         self.tables[child] = list(self.tables[parent])
         self.lengths[child] = self.lengths[parent]
@@ -219,9 +307,15 @@ class BlockManagerModel:
         if seq not in self.tables:
             raise KeyError(seq)
         row = self.tables[seq]
-        for blk in (reversed(row) if self.caching else row):
-            if blk >= 0:
-                self._release(blk)
+        if seq in self.swapped:
+            for h in row:
+                if h >= 0:
+                    self.host_refcount[h] -= 1
+                    if self.host_refcount[h] == 0:
+                        self.host_stack.append(h)
+            self.swapped.discard(seq)
+        else:
+            self._release_all(row)
         del self.tables[seq]
         del self.lengths[seq]
         del self.tokens[seq]
@@ -232,8 +326,9 @@ class BlockManagerModel:
         overwritten: KV outside a sliding window can be dropped).  The last block is
         always kept (it holds the newest token).  Dropped entries become -1.  Returns the
         number of entries dropped now."""
-        if seq not in self.tables or token < 0:
+        if token < 0:
             raise KeyError(seq)
+        self._check_resident(seq)
         table = self.tables[seq]
         whole = [j for j in range(len(table) - 1) if (j + 1) * self.block_size <= token]
         dropped = 0
@@ -250,6 +345,7 @@ class BlockManagerModel:
         """``(tables, context_lens)``: ``[n][max_blocks]`` padded with -1, and lengths."""
         tables, lens = [], []
         for seq in seqs:
+            self._check_resident(seq)
             row = self.tables[seq]
             if len(row) > max_blocks:
                 raise ValueError("max_blocks too small")
@@ -260,13 +356,20 @@ class BlockManagerModel:
     # -- invariants --------------------------------------------------------------
     def check_invariants(self):
         """Conservation of references and of blocks; raises AssertionError if broken."""
-        held = {}
-        for row in self.tables.values():
+        held, host_held = {}, {}
+        for seq, row in self.tables.items():
+            where = host_held if seq in self.swapped else held
             for blk in row:
                 if blk >= 0:
-                    held[blk] = held.get(blk, 0) + 1
+                    where[blk] = where.get(blk, 0) + 1
         for blk in range(self.num_blocks):
             assert self.refcount[blk] == held.get(blk, 0), blk
+        for h in range(len(self.host_refcount)):
+            assert self.host_refcount[h] == host_held.get(h, 0), h
+        hfree = set(self.host_stack)
+        assert len(hfree) == len(self.host_stack)
+        assert all(self.host_refcount[h] == 0 for h in hfree)
+        assert len(hfree) + sum(1 for r in self.host_refcount if r > 0) == len(self.host_refcount)
         free = set(self.stack)
         assert len(free) == len(self.stack), "a block is on the free stack twice"
         assert all(self.refcount[b] == 0 for b in free)

@@ -78,6 +78,14 @@ _SIGNATURES = {
                                                   _PI32]),
     "pa_block_state": (ctypes.c_int, [_P, _I32, _PI32]),
     "pa_export_evictable": (ctypes.c_int, [_P, _PI32, _I32, _PI32]),
+    "pa_swap_space_bytes": (_I64, [ctypes.POINTER(PoolDesc), _I32]),
+    "pa_pool_set_swap_space": (ctypes.c_int, [_P, _I32]),
+    "pa_seq_swap_out": (ctypes.c_int, [_P, _PI32, _I32, _PI32, _I32, _PI32]),
+    "pa_seq_swap_in": (ctypes.c_int, [_P, _PI32, _I32, _PI32, _I32, _PI32]),
+    "pa_seq_swapped": (ctypes.c_int, [_P, _I32, _PI32]),
+    "pa_host_block_refcount": (ctypes.c_int, [_P, _I32, _PI32]),
+    "pa_export_host_free_stack": (ctypes.c_int, [_P, _PI32, _I32, _PI32]),
+    "pa_swap_blocks": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _I32, _P]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 
@@ -299,6 +307,67 @@ def pa_export_evictable(pool):
     n = ctypes.c_int32()
     _check(lib().pa_export_evictable(pool.handle, _i32p(out), cap, ctypes.byref(n)))
     return out[:n.value]
+
+
+def pa_swap_space_bytes(desc, host_blocks):
+    return _check(lib().pa_swap_space_bytes(ctypes.byref(desc), host_blocks))
+
+
+def pa_pool_set_swap_space(pool, host_blocks):
+    _check(lib().pa_pool_set_swap_space(pool.handle, host_blocks))
+    pool.num_host_blocks = host_blocks
+
+
+def _swap(fn, pool, seqs):
+    seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+    cap = max(1, getattr(pool, "num_host_blocks", 0), pool.num_blocks)
+    pairs = np.zeros(2 * cap, dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(fn(pool.handle, _i32p(seqs if len(seqs) else np.zeros(1, np.int32)), len(seqs),
+              _i32p(pairs), cap, ctypes.byref(n)))
+    return [(int(pairs[2 * i]), int(pairs[2 * i + 1])) for i in range(n.value)]
+
+
+def pa_seq_swap_out(pool, seqs):
+    """Returns the (device block, host block) pairs to copy."""
+    return _swap(lib().pa_seq_swap_out, pool, seqs)
+
+
+def pa_seq_swap_in(pool, seqs):
+    """Returns the (host block, device block) pairs to copy."""
+    return _swap(lib().pa_seq_swap_in, pool, seqs)
+
+
+def pa_seq_swapped(pool, seq):
+    out = ctypes.c_int32()
+    _check(lib().pa_seq_swapped(pool.handle, seq, ctypes.byref(out)))
+    return bool(out.value)
+
+
+def pa_host_block_refcount(pool, host_block):
+    rc = ctypes.c_int32()
+    _check(lib().pa_host_block_refcount(pool.handle, host_block, ctypes.byref(rc)))
+    return rc.value
+
+
+def pa_export_host_free_stack(pool):
+    cap = max(1, getattr(pool, "num_host_blocks", 0))
+    out = np.zeros(cap, dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(lib().pa_export_host_free_stack(pool.handle, _i32p(out), cap, ctypes.byref(n)))
+    return out[:n.value]
+
+
+def pa_swap_blocks(pool, host, pairs, to_host, stream=None):
+    """host: pinned CPU tensor (the swap space); pairs: GPU int32 ``[n][2]``."""
+    import torch
+    if host.device.type != "cpu" or not host.is_pinned():
+        raise ValueError("the swap space must be a pinned CPU tensor")
+    n = pairs.shape[0] if pairs.numel() else 0
+    _check(lib().pa_swap_blocks(pool.handle, ctypes.c_void_p(host.data_ptr()),
+                                host.numel() * host.element_size(),
+                                _dev(pairs, torch.int32, "pairs") if n else None, n,
+                                1 if to_host else 0, _stream(stream)))
 
 
 def pa_seq_fork(pool, parent):

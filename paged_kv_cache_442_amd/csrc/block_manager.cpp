@@ -183,7 +183,7 @@ MgrStatus BlockManager::seq_new_prefix(const int32_t* prompt, int32_t n_prompt, 
 
 MgrStatus BlockManager::seq_append(int32_t seq, int32_t n, const int32_t* tokens, int64_t* slots,
                                    int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow) {
-  if (!live(seq) || n < 0) return MgrStatus::invalid;
+  if (!live(seq) || n < 0 || seqs_[seq].swapped) return MgrStatus::invalid;
   Seq& s = seqs_[seq];
   const int64_t L = s.length;
   if (L + n > INT32_MAX) return MgrStatus::range;
@@ -244,7 +244,7 @@ MgrStatus BlockManager::seq_append_batch(const int32_t* seqs, int32_t count, con
   for (int32_t i = 0; i < count; ++i) {
     const int32_t s = seqs[i];
     const int32_t k = n ? n[i] : 1;
-    if (!live(s) || k < 0 || seen.count(s)) return MgrStatus::invalid;
+    if (!live(s) || k < 0 || seen.count(s) || seqs_[s].swapped) return MgrStatus::invalid;
     seen[s] = 1;
     const Seq& q = seqs_[s];
     const int64_t L = q.length;
@@ -276,7 +276,7 @@ MgrStatus BlockManager::seq_append_batch(const int32_t* seqs, int32_t count, con
 }
 
 MgrStatus BlockManager::seq_release_before(int32_t seq, int32_t token, int32_t* released) {
-  if (!live(seq) || token < 0) return MgrStatus::invalid;
+  if (!live(seq) || token < 0 || seqs_[seq].swapped) return MgrStatus::invalid;
   Seq& s = seqs_[seq];
   // Block j holds tokens [j * bs, (j + 1) * bs); it is wholly before `token` when
   // (j + 1) * bs <= token.  The last block of a sequence stays whatever `token` is.
@@ -295,7 +295,7 @@ MgrStatus BlockManager::seq_release_before(int32_t seq, int32_t token, int32_t* 
 }
 
 MgrStatus BlockManager::seq_fork(int32_t parent, int32_t* child) {
-  if (!live(parent)) return MgrStatus::invalid;
+  if (!live(parent) || seqs_[parent].swapped) return MgrStatus::invalid;
   int32_t id;
   MgrStatus st = seq_new(&id);
   if (st != MgrStatus::ok) return st;
@@ -317,13 +317,116 @@ MgrStatus BlockManager::seq_free(int32_t seq) {
   if (!live(seq)) return MgrStatus::invalid;
   Seq& s = seqs_[seq];
   const size_t nb = s.table.size();
-  for (size_t i = 0; i < nb; ++i) {
-    const int32_t b = s.table[caching_ ? nb - 1 - i : i];  // last to first when caching
-    if (b >= 0) release(b);
+  if (s.swapped) {
+    for (int32_t h : s.table)
+      if (h >= 0 && --host_refcount_[h] == 0) host_free_.push_back(h);
+  } else {
+    for (size_t i = 0; i < nb; ++i) {
+      const int32_t b = s.table[caching_ ? nb - 1 - i : i];  // last to first when caching
+      if (b >= 0) release(b);
+    }
   }
   if (s.node >= 0) unref(s.node);
   s = Seq();
   return MgrStatus::ok;
+}
+
+// ------------------------------------------------------------------ swap
+
+MgrStatus BlockManager::set_swap_space(int32_t host_blocks) {
+  if (host_blocks < 0) return MgrStatus::invalid;
+  for (const Seq& s : seqs_)
+    if (s.live && s.swapped) return MgrStatus::invalid;
+  host_refcount_.assign(host_blocks, 0);
+  host_free_.clear();
+  for (int32_t i = host_blocks - 1; i >= 0; --i) host_free_.push_back(i);  // 0 first
+  return MgrStatus::ok;
+}
+
+MgrStatus BlockManager::seq_swap_out(const int32_t* seqs, int32_t count, int32_t* pairs,
+                                     int32_t cap, int32_t* n_pairs) {
+  std::unordered_map<int32_t, int32_t> to_host;  // device block -> host block
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t q = seqs[i];
+    if (!live(q) || seqs_[q].swapped) return MgrStatus::invalid;
+    for (int32_t k = 0; k < i; ++k)
+      if (seqs[k] == q) return MgrStatus::invalid;
+    for (int32_t b : seqs_[q].table)
+      if (b >= 0) to_host.emplace(b, -1);
+  }
+  const int64_t need = static_cast<int64_t>(to_host.size());
+  if (need > cap) return MgrStatus::range;
+  if (need > static_cast<int64_t>(host_free_.size())) return MgrStatus::no_blocks;
+
+  int32_t made = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    Seq& s = seqs_[seqs[i]];
+    const std::vector<int32_t> device = s.table;
+    for (int32_t& e : s.table) {
+      if (e < 0) continue;
+      int32_t& h = to_host[e];
+      if (h < 0) {
+        h = host_free_.back();
+        host_free_.pop_back();
+        pairs[2 * made] = e;
+        pairs[2 * made + 1] = h;
+        ++made;
+      }
+      host_refcount_[h] += 1;
+      e = h;
+    }
+    const size_t nb = device.size();
+    for (size_t k = 0; k < nb; ++k) {
+      const int32_t b = device[caching_ ? nb - 1 - k : k];  // as a free would
+      if (b >= 0) release(b);
+    }
+    s.swapped = true;
+  }
+  *n_pairs = made;
+  return MgrStatus::ok;
+}
+
+MgrStatus BlockManager::seq_swap_in(const int32_t* seqs, int32_t count, int32_t* pairs,
+                                    int32_t cap, int32_t* n_pairs) {
+  std::unordered_map<int32_t, int32_t> to_device;  // host block -> device block
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t q = seqs[i];
+    if (!live(q) || !seqs_[q].swapped) return MgrStatus::invalid;
+    for (int32_t k = 0; k < i; ++k)
+      if (seqs[k] == q) return MgrStatus::invalid;
+    for (int32_t h : seqs_[q].table)
+      if (h >= 0) to_device.emplace(h, -1);
+  }
+  const int64_t need = static_cast<int64_t>(to_device.size());
+  if (need > cap) return MgrStatus::range;
+  if (need > static_cast<int64_t>(num_free())) return MgrStatus::no_blocks;
+
+  int32_t made = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    Seq& s = seqs_[seqs[i]];
+    const std::vector<int32_t> host = s.table;
+    for (int32_t& e : s.table) {
+      if (e < 0) continue;
+      int32_t& b = to_device[e];
+      if (b < 0) {
+        b = pop();
+        pairs[2 * made] = e;
+        pairs[2 * made + 1] = b;
+        ++made;
+      }
+      refcount_[b] += 1;
+      e = b;
+    }
+    for (int32_t h : host)
+      if (h >= 0 && --host_refcount_[h] == 0) host_free_.push_back(h);
+    s.swapped = false;
+  }
+  *n_pairs = made;
+  return MgrStatus::ok;
+}
+
+void BlockManager::host_free_stack_top_first(std::vector<int32_t>* out) const {
+  out->assign(host_free_.rbegin(), host_free_.rend());
 }
 
 void BlockManager::free_stack_top_first(std::vector<int32_t>* out) const {

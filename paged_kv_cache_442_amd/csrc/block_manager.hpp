@@ -29,6 +29,16 @@
 //     to the first, so a sequence's tail is evicted before its prefix.
 // Identities are interned exactly (a trie of block-sized token runs), so equal prefixes
 // always meet and different ones never do.
+//
+// Swap preemption ("vLLM explained", table on when KV may be overwritten: when memory
+// runs short a request is preempted, its KV recomputed later or moved to CPU memory).
+// A swap space of host blocks has its own LIFO free stack and reference counts.
+// Swapping a set of sequences out gives every distinct device block in their tables one
+// host block (a block shared by several of them is copied once), reports the (device,
+// host) pairs to copy, points the tables at the host blocks and drops the sequences'
+// device references as a free would.  Swapping in is the mirror image, taking device
+// blocks as an append does (empty first, then eviction).  A swapped-out sequence can
+// only be swapped in or freed.
 #pragma once
 
 #include <cstdint>
@@ -74,6 +84,21 @@ class BlockManager {
   // that has moved past them); their table entries become -1.  Sets *released.
   MgrStatus seq_release_before(int32_t seq, int32_t token, int32_t* released);
 
+  // Swap space of `host_blocks` blocks (only while no sequence is swapped out).
+  MgrStatus set_swap_space(int32_t host_blocks);
+  // Moves seqs[0..count) (distinct, live, resident) to host blocks; pairs (device,
+  // host) in order of first use; all-or-nothing.
+  MgrStatus seq_swap_out(const int32_t* seqs, int32_t count, int32_t* pairs, int32_t cap,
+                         int32_t* n_pairs);
+  // Moves seqs[0..count) (distinct, live, swapped out) back to device blocks; pairs
+  // (host, device); all-or-nothing.
+  MgrStatus seq_swap_in(const int32_t* seqs, int32_t count, int32_t* pairs, int32_t cap,
+                        int32_t* n_pairs);
+  bool swapped(int32_t seq) const { return live(seq) && seqs_[seq].swapped; }
+  int32_t num_host_blocks() const { return static_cast<int32_t>(host_refcount_.size()); }
+  int32_t host_refcount(int32_t h) const { return host_refcount_[h]; }
+  void host_free_stack_top_first(std::vector<int32_t>* out) const;
+
   bool live(int32_t seq) const;
   int32_t length(int32_t seq) const { return seqs_[seq].length; }
   const std::vector<int32_t>& table(int32_t seq) const { return seqs_[seq].table; }
@@ -91,6 +116,7 @@ class BlockManager {
  private:
   struct Seq {
     bool live = false;
+    bool swapped = false;      // table holds host blocks
     bool tracked = true;       // every token's id is known (prefix caching)
     int32_t length = 0;
     int64_t node = -1;         // identity node of the last full block (-1: none yet)
@@ -122,6 +148,9 @@ class BlockManager {
   std::vector<int32_t> free_stack_;  // back() is handed out next
   std::vector<int32_t> refcount_;
   std::vector<Seq> seqs_;            // index = sequence id
+
+  std::vector<int32_t> host_free_;       // back() is handed out next
+  std::vector<int32_t> host_refcount_;
 
   bool caching_ = false;
   std::vector<int64_t> node_of_block_;       // identity a block is cached under, or -1

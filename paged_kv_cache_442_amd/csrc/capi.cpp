@@ -380,6 +380,7 @@ int pa_export_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n, 
     return fail(PA_E_INVAL, "seqs, tables_out and ctx_out must be non-NULL");
   for (int32_t i = 0; i < n; ++i) {
     if (!pool->mgr->live(seqs[i])) return fail(PA_E_INVAL, "unknown or freed sequence %d", seqs[i]);
+    if (pool->mgr->swapped(seqs[i])) return fail(PA_E_INVAL, "sequence %d is swapped out", seqs[i]);
     if (static_cast<int64_t>(pool->mgr->table(seqs[i]).size()) > max_blocks)
       return fail(PA_E_RANGE, "sequence %d holds %zu blocks > max_blocks %d", seqs[i],
                   pool->mgr->table(seqs[i]).size(), max_blocks);
@@ -644,6 +645,101 @@ int pa_seq_release_before(pa_pool* pool, int32_t seq, int32_t token, int32_t* n_
   int st = mgr_status(pool->mgr->seq_release_before(seq, token, &n), "pa_seq_release_before");
   if (st == PA_OK) *n_released_out = n;
   return st;
+}
+
+int64_t pa_swap_space_bytes(const pa_pool_desc* desc, int32_t host_blocks) {
+  if (host_blocks < 0) return fail(PA_E_INVAL, "host_blocks < 0");
+  const int64_t b = pa_block_bytes(desc);
+  if (b < 0) return b;
+  return b * host_blocks;
+}
+
+int pa_pool_set_swap_space(pa_pool* pool, int32_t host_blocks) {
+  if (!pool) return fail(PA_E_INVAL, "pool is NULL");
+  if (pool->mgr->set_swap_space(host_blocks) != pa::MgrStatus::ok)
+    return fail(PA_E_INVAL, "pa_pool_set_swap_space: bad size, or sequences are swapped out");
+  return ok();
+}
+
+static int swap_call(pa_pool* pool, const int32_t* seqs, int32_t count, int32_t* pairs_out,
+                     int32_t cap, int32_t* n_pairs_out, bool out, const char* what) {
+  if (!pool || !n_pairs_out) return fail(PA_E_INVAL, "%s: pool and n_pairs_out must be non-NULL", what);
+  if (count < 0 || (count > 0 && !seqs)) return fail(PA_E_INVAL, "%s: bad seqs / count", what);
+  if (cap < 0 || (cap > 0 && !pairs_out)) return fail(PA_E_INVAL, "%s: bad pairs_out / cap", what);
+  int32_t n = 0;
+  const pa::MgrStatus st = out ? pool->mgr->seq_swap_out(seqs, count, pairs_out, cap, &n)
+                               : pool->mgr->seq_swap_in(seqs, count, pairs_out, cap, &n);
+  const int rc = mgr_status(st, what);
+  if (rc == PA_OK) *n_pairs_out = n;
+  return rc;
+}
+
+int pa_seq_swap_out(pa_pool* pool, const int32_t* seqs, int32_t count, int32_t* pairs_out,
+                    int32_t cap, int32_t* n_pairs_out) {
+  return swap_call(pool, seqs, count, pairs_out, cap, n_pairs_out, true, "pa_seq_swap_out");
+}
+
+int pa_seq_swap_in(pa_pool* pool, const int32_t* seqs, int32_t count, int32_t* pairs_out,
+                   int32_t cap, int32_t* n_pairs_out) {
+  return swap_call(pool, seqs, count, pairs_out, cap, n_pairs_out, false, "pa_seq_swap_in");
+}
+
+int pa_seq_swapped(const pa_pool* pool, int32_t seq, int32_t* swapped_out) {
+  if (!pool || !swapped_out) return fail(PA_E_INVAL, "pool and swapped_out must be non-NULL");
+  if (!pool->mgr->live(seq)) return fail(PA_E_INVAL, "unknown or freed sequence %d", seq);
+  *swapped_out = pool->mgr->swapped(seq) ? 1 : 0;
+  return ok();
+}
+
+int pa_host_block_refcount(const pa_pool* pool, int32_t host_block, int32_t* rc_out) {
+  if (!pool || !rc_out) return fail(PA_E_INVAL, "pool and rc_out must be non-NULL");
+  if (host_block < 0 || host_block >= pool->mgr->num_host_blocks())
+    return fail(PA_E_INVAL, "host block %d out of range", host_block);
+  *rc_out = pool->mgr->host_refcount(host_block);
+  return ok();
+}
+
+int pa_export_host_free_stack(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out) {
+  if (!pool || !n_out || cap < 0 || (cap > 0 && !out)) return fail(PA_E_INVAL, "bad arguments");
+  std::vector<int32_t> v;
+  pool->mgr->host_free_stack_top_first(&v);
+  *n_out = static_cast<int32_t>(v.size());
+  if (static_cast<int64_t>(v.size()) > cap) return fail(PA_E_RANGE, "cap %d < %zu free host blocks", cap, v.size());
+  for (size_t i = 0; i < v.size(); ++i) out[i] = v[i];
+  return ok();
+}
+
+int pa_swap_blocks(pa_pool* pool, void* host_base, int64_t host_bytes, const int32_t* pairs,
+                   int32_t n_pairs, int32_t to_host, void* stream) {
+  int st = check_device_pool(pool, 0);
+  if (st) return st;
+  if (n_pairs < 0) return fail(PA_E_INVAL, "n_pairs < 0");
+  if (n_pairs == 0) return ok();
+  if (!pairs || !host_base) return fail(PA_E_INVAL, "pairs and host_base must be non-NULL");
+  const int32_t host_blocks = pool->mgr->num_host_blocks();
+  if (host_blocks == 0) return fail(PA_E_INVAL, "pa_swap_blocks: the pool has no swap space");
+  const int64_t need = pa_block_bytes(&pool->desc) * host_blocks;
+  if (host_bytes < need)
+    return fail(PA_E_INVAL, "host buffer holds %lld bytes < %lld of the swap space",
+                static_cast<long long>(host_bytes), static_cast<long long>(need));
+  if (reinterpret_cast<uintptr_t>(host_base) % 16 != 0) return fail(PA_E_INVAL, "host_base not 16-byte aligned");
+  if (2 * pool->desc.num_layers > 65535) return fail(PA_E_UNSUPPORTED, "too many layers");
+  const int64_t block_bytes = pool->array_bytes / pool->desc.num_blocks;
+  if (block_bytes % 16 != 0) return fail(PA_E_UNSUPPORTED, "per-layer block bytes not a multiple of 16");
+  // The kernel reaches the host buffer through its device mapping; memory that is not
+  // pinned host memory has none and is rejected here, before any launch.
+  void* mapped = nullptr;
+  if (hipHostGetDevicePointer(&mapped, host_base, 0) != hipSuccess || !mapped) {
+    (void)hipGetLastError();
+    return fail(PA_E_INVAL, "pa_swap_blocks: host_base is not pinned host memory");
+  }
+  const int32_t N = pool->desc.num_blocks;
+  const hipError_t e = to_host
+      ? pa::launch_swap_blocks(pairs, n_pairs, pool->dev_base, N, mapped, host_blocks,
+                               2 * pool->desc.num_layers, block_bytes, static_cast<hipStream_t>(stream))
+      : pa::launch_swap_blocks(pairs, n_pairs, mapped, host_blocks, pool->dev_base, N,
+                               2 * pool->desc.num_layers, block_bytes, static_cast<hipStream_t>(stream));
+  return hip_status(e, "pa_swap_blocks");
 }
 
 int pa_pool_set_kv_scales(pa_pool* pool, int32_t layer, float k_scale, float v_scale) {

@@ -863,6 +863,35 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* __restr
   for (; c < block_chunks; c += 256) d[c] = s[c];
 }
 
+// blockIdx.x = pair, blockIdx.y = array: block pairs[2x] of the source side to block
+// pairs[2x + 1] of the destination side, where the two sides are the device pool and
+// the host swap space (same layout, their own block counts).  The host side is pinned
+// host memory read or written through its device mapping, so one launch moves every
+// block over the host link ("vLLM explained", table on when KV may be overwritten:
+// preemption by swapping to CPU memory).
+__global__ __launch_bounds__(256) void swap_blocks_kernel(const int32_t* __restrict__ pairs,
+                                                          const u32x4* src_base, int32_t src_blocks,
+                                                          u32x4* dst_base, int32_t dst_blocks,
+                                                          int64_t block_chunks) {
+  const int32_t src = pairs[2 * blockIdx.x];
+  const int32_t dst = pairs[2 * blockIdx.x + 1];
+  if (static_cast<unsigned>(src) >= static_cast<unsigned>(src_blocks) ||
+      static_cast<unsigned>(dst) >= static_cast<unsigned>(dst_blocks))
+    return;
+  const u32x4* s = src_base + (static_cast<int64_t>(blockIdx.y) * src_blocks + src) * block_chunks;
+  u32x4* d = dst_base + (static_cast<int64_t>(blockIdx.y) * dst_blocks + dst) * block_chunks;
+  constexpr int kUnroll = 4;
+  int64_t c = threadIdx.x;
+  for (; c + (kUnroll - 1) * 256 < block_chunks; c += kUnroll * 256) {
+    u32x4 x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) x[u] = s[c + u * 256];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) d[c + u * 256] = x[u];
+  }
+  for (; c < block_chunks; c += 256) d[c] = s[c];
+}
+
 template <class E, int GW, int HS>
 hipError_t launch_persistent(const DecodeArgs& a, hipStream_t s) {
   // Workgroups resident at once on the current device (cached per device).
@@ -956,6 +985,17 @@ hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, const int6
                      static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), slots,
                      static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), total,
                      num_kv_heads, block_size, num_slots, inv_k, inv_v);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(const int32_t* pairs, int32_t n_pairs, const void* src_base,
+                              int32_t src_blocks, void* dst_base, int32_t dst_blocks, int32_t arrays,
+                              int64_t block_bytes, hipStream_t s) {
+  (void)hipGetLastError();
+  if (n_pairs == 0) return hipSuccess;
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(n_pairs, arrays), dim3(256), 0, s, pairs,
+                     static_cast<const u32x4*>(src_base), src_blocks, static_cast<u32x4*>(dst_base),
+                     dst_blocks, block_bytes / 16);
   return hipGetLastError();
 }
 

@@ -58,6 +58,11 @@ hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, const int6
 
 // base: pool base, holding `arrays` (= 2 * num_layers) arrays, each of num_blocks blocks of
 // block_bytes bytes (one layer's K or V part of a block).
+// Whole-block copies between the device pool and a host swap space (pinned host memory
+// addressed through its device mapping); pairs are device int32 [n_pairs][2].
+hipError_t launch_swap_blocks(const int32_t* pairs, int32_t n_pairs, const void* src_base,
+                              int32_t src_blocks, void* dst_base, int32_t dst_blocks, int32_t arrays,
+                              int64_t block_bytes, hipStream_t s);
 hipError_t launch_copy_blocks(const int32_t* pairs, int32_t n_pairs, void* base, int32_t arrays,
                               int32_t num_blocks, int64_t block_bytes, hipStream_t s);
 
