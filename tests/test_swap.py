@@ -255,6 +255,8 @@ def test_swap_round_trip_is_bit_exact_and_decode_after_swap_in(dtype, layers):
     lens = [1, 15, 16, 17, 100, 257, 600, 1000]
     w = wl.custom_decode(31 + dtype, dtype, lens, 16, 4, block_size=16, num_blocks=200)
     sess = DecodeSession(w, num_layers=layers, layer=layers - 1)
+    sess.write_new_tokens()                     # each sequence's newest token too
+    torch.cuda.synchronize()
     pool = sess.pool
     M = 96
     pa.pa_pool_set_swap_space(pool, M)
