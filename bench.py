@@ -33,6 +33,9 @@ WORKLOADS = {
     "mixed_chunked": "Mixed batch, one layer: 8 prefill chunks of 256-512 causal query rows over "
                      "cached prefixes of 0-4096 tokens plus 96 decode rows of 1-4096 tokens; GQA "
                      "32/8, d 128, bf16, block 32",
+    "shared_prefix": "Parallel sampling, one layer: 32 groups x 4 branches forked from a 1024-token "
+                     "prompt plus 1-15 decoded tokens, tails of 1-256 tokens, GQA 32/8, d 128, bf16, "
+                     "block 16; 96 copy-on-write block copies, then decode of the 128 branches",
     "swap": "Swap preemption, one Llama-3-70B-shaped layer (the llama3_70b cache): every 4th of "
             "the 128 sequences swapped out to pinned host memory and back in",
     "prefix_cache": "Prefix caching, one layer: 256 requests served in order over 8 system prompts "
@@ -192,6 +195,8 @@ def main():
         return bench_prefix_cache(args, torch)
     if args.workload == "swap":
         return bench_swap(args, torch)
+    if args.workload == "shared_prefix":
+        return bench_shared_prefix(args, torch)
 
     t0 = time.perf_counter()
     w = make_workload(args.workload, args.num_q_heads, args.fixed_len)
@@ -468,6 +473,88 @@ def bench_mixed(args, torch):
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_shared_prefix(args, torch):
+    """Parallel sampling: decode of 128 branches whose tables share their group's context
+    blocks, and the 96 copy-on-write block copies.  Logical bytes count every branch's
+    tokens; unique bytes count each distinct block once."""
+    from paged_kv_cache_442_amd import workloads as wl
+    from paged_kv_cache_442_amd.session import SharedPrefixSession
+    from oracle import attention, fpbits
+
+    w = wl.shared_prefix()
+    sess = SharedPrefixSession(w)
+    torch.cuda.synchronize()
+    e, Hq, Hkv, d, bs = 2, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    S = len(sess.seqs)
+    B = int(np.sum(sess.lens)) * Hkv * d * 2 * e + S * Hq * d * e
+    t = sess.tables_host
+    B_unique = int(np.unique(t[t >= 0]).size) * bs * Hkv * d * 2 * e + S * Hq * d * e
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        sess.decode()
+    torch.cuda.synchronize()
+    n = args.steps
+    dec = [(ev(), ev()) for _ in range(n)]
+    for i in range(n):
+        dec[i][0].record(stream)
+        sess.decode()
+        dec[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in dec]))
+    # The copies again, from the same sources into free blocks: the real destinations now
+    # hold the branches' own tokens and must not be overwritten.
+    from paged_kv_cache_442_amd import binding as pa
+    free = pa.pa_export_free_stack(sess.pool)[:len(sess.cow_pairs)]
+    timing_pairs = torch.tensor([(s_, int(f)) for (s_, _), f in zip(sess.cow_pairs, free)],
+                                dtype=torch.int32, device="cuda")
+    for _ in range(args.warmup):
+        pa.pa_copy_blocks(sess.pool, timing_pairs)
+    cp = [(ev(), ev()) for _ in range(n)]
+    for i in range(n):
+        cp[i][0].record(stream)
+        pa.pa_copy_blocks(sess.pool, timing_pairs)
+        cp[i][1].record(stream)
+    torch.cuda.synchronize()
+    cp_ms = float(np.mean([a.elapsed_time(b) for a, b in cp]))
+    copy_bytes = 2 * len(sess.cow_pairs) * pa_block_bytes_of(sess)
+    got = sess.out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for idx in (0, S - 1):
+        s_ = sess.seqs[idx]
+        kt, vt = sess.branch_tokens(s_)
+        want = attention.contiguous_decode(w.dtype, w.q[sess.branch_of[s_]], fpbits.decode(w.dtype, kt),
+                                           fpbits.decode(w.dtype, vt), attention.default_scale(d))
+        worst = max(worst, float(np.max(np.abs(got[idx] - want))))
+    value = B / (dec_ms * 1e-3) / 1e9
+    line = {
+        "metric": "paged-decode KV GB/s and % of HBM peak at 1 MI355X; tokens/sec per layer",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": round(dec_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/Q, seeded block permutation)",
+        "config": {"workload": "shared_prefix", "description": WORKLOADS["shared_prefix"],
+                   "branches": S, "cow_pairs": len(sess.cow_pairs), "num_blocks": w.num_blocks,
+                   "logical_bytes_per_step": B, "unique_bytes_per_step": B_unique},
+        "tokens_per_s_per_layer": round(S / (dec_ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (plan + partitions + merge)",
+                     "achieved": round(value, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "note": "logical bytes; the unique set (unique_bytes_per_step) is read once "
+                             "per branch, mostly from cache"},
+        "unique_GBps": round(B_unique / (dec_ms * 1e-3) / 1e9, 2),
+        "copy_blocks": {"pairs": len(sess.cow_pairs), "ms": round(cp_ms, 5),
+                        "GBps_read_plus_write": round(copy_bytes / (cp_ms * 1e-3) / 1e9, 2)},
+        "max_abs_err_sampled": worst, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def pa_block_bytes_of(sess):
+    from paged_kv_cache_442_amd import binding as pa
+    return pa.pa_block_bytes(sess.desc)
 
 
 def bench_swap(args, torch):

@@ -583,8 +583,8 @@ int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_
     return fail(PA_E_UNSUPPORTED, "head_dim %d (supported: %d)", d.head_dim, pa::kHeadDim);
   if (d.kv_dtype != PA_F16 && d.kv_dtype != PA_BF16)
     return fail(PA_E_UNSUPPORTED, "chunked prefill runs on the matrix cores: fp16 or bf16 caches only");
-  if (d.block_size % 16 != 0)
-    return fail(PA_E_UNSUPPORTED, "block_size %d (must be a multiple of 16)", d.block_size);
+  if (d.block_size < 16 || (d.block_size & (d.block_size - 1)) != 0)
+    return fail(PA_E_UNSUPPORTED, "block_size %d (chunked prefill: a power of two >= 16)", d.block_size);
   if (!std::isfinite(scale)) return fail(PA_E_INVAL, "scale is not finite");
   if (num_seqs == 0 || max_query_len == 0) return ok();
   if (!q || !query_start || !block_tables || !context_lens || !out)
@@ -611,6 +611,7 @@ int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_
   a.max_blocks = max_blocks;
   a.num_blocks = d.num_blocks;
   a.block_size = d.block_size;
+  a.block_shift = __builtin_ctz(static_cast<unsigned>(d.block_size));
   a.max_context = max_context;
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(pa::launch_prefill(a, static_cast<int>(d.kv_dtype), group, max_query_len,

@@ -39,6 +39,7 @@ constexpr int kCols = 128;    // (row, head) columns per workgroup
 constexpr int kKRow = kHead + 8;   // K tile row stride in LDS (elements), against bank conflicts
 constexpr int kVRow = kKeys + 8;   // transposed V tile row stride (elements)
 constexpr float kRescaleSlack = 8.0f;
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters left alone
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -73,9 +74,13 @@ template <class M, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   using T = typename M::elem;
   constexpr int TR = kCols / G;  // query rows per workgroup
+  constexpr int kTileK = kKeys * kKRow;
+  constexpr int kTileV = kHead * kVRow;
 
-  __shared__ __align__(16) T s_k[kKeys * kKRow];   // K tile, [key][dim]
-  __shared__ __align__(16) T s_vt[kHead * kVRow];  // V tile transposed, [dim][key]
+  // Two buffers of each tile: while one is read, the next tile is stored into the other,
+  // so a tile costs one barrier.
+  __shared__ __align__(16) T s_k[2 * kTileK];   // K tile, [key][dim]
+  __shared__ __align__(16) T s_vt[2 * kTileV];  // V tile transposed, [dim][key]
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -83,7 +88,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int half = lane / 32;  // which 8 of a 16-dim slice, which 4 keys of 8
   const int seq = blockIdx.y;
   const int kvh = blockIdx.z;
-  const int r0 = blockIdx.x * TR;
+  // Row blocks go last to first: a chunk's last rows see the most keys, so the longest
+  // workgroups start first.
+  const int r0 = (gridDim.x - 1 - blockIdx.x) * TR;
 
   const int qs = a.query_start[seq];
   const int n_rows = a.query_start[seq + 1] - qs;
@@ -100,6 +107,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int row = r0 + col % TR;
   const bool col_ok = row < n_rows;
   const int pos = L - n_rows + row;  // the row's position; it sees keys 0 .. pos
+  // The wave's first row: no column of the wave sees fewer keys than it.
+  const int pos_min = L - n_rows + r0 + (TR >= 32 ? (32 * wave) % TR : 0);
   const int64_t out_row = (static_cast<int64_t>(qs) + row) * a.num_q_heads + kvh * G + hh;
 
   if (bad) {
@@ -125,42 +134,50 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int kmax = L - n_rows + min(r0 + TR, n_rows) - 1;
   const int n_tiles = kmax / kKeys + 1;
 
-  // Staging: thread t moves 16-byte chunk t % 16 of keys 2 (t / 16) and 2 (t / 16) + 1.
-  const int sc = tid % 16;
-  const int sk = 2 * (tid / 16);
+  // Staging: thread t moves 16-byte chunk t / 16 of keys 2 (t % 16) and 2 (t % 16) + 1
+  // (one block: block sizes are powers of two >= 16).  The 16 threads of a chunk hold 16
+  // key pairs, so their stores into the transposed V tile are 16 consecutive dwords of
+  // one row (distinct banks), and each global load still reads 64 contiguous bytes of
+  // every key it touches.  Every load below is issued whatever the key: keys past kmax
+  // read an in-bounds row and are zeroed when staged, so the loads of a tile always
+  // number the same and the waits before using them stay exact.
+  const int sk = 2 * (tid % 16);
+  const int sc = tid / 16;
   const int32_t* tbl = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
-  const int64_t row_elems = kHead;
   const int64_t run_elems = static_cast<int64_t>(a.block_size) * kHead;
+  const int sh = a.block_shift;
+  const int bmask = a.block_size - 1;
   bool bad_blk = false;
-  u32x4 kst[2], vst[2];
-  auto load_tile = [&](int t0) {
+  auto tile_block = [&](int t) -> int { return tbl[min(t * kKeys + sk, kmax) >> sh]; };
+  auto issue = [&](int t, int phys, u32x4 (&kr)[2], u32x4 (&vr)[2], int& valid) {
+    const int key = t * kKeys + sk;
+    valid = (key <= kmax ? 1 : 0) | (key + 1 <= kmax ? 2 : 0);
+    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(a.num_blocks)) {
+      bad_blk |= key <= kmax;
+      phys = 0;
+    }
+    const int64_t base = (static_cast<int64_t>(phys) * a.num_kv_heads + kvh) * run_elems + sc * 8;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int t = t0 + sk + j;
-      kst[j] = vst[j] = u32x4{0u, 0u, 0u, 0u};
-      if (t <= kmax) {
-        int phys = tbl[t / a.block_size];
-        if (static_cast<unsigned>(phys) >= static_cast<unsigned>(a.num_blocks)) {
-          bad_blk = true;
-          phys = 0;
-        }
-        const int64_t off = (static_cast<int64_t>(phys) * a.num_kv_heads + kvh) * run_elems +
-                            static_cast<int64_t>(t % a.block_size) * row_elems + sc * 8;
-        kst[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.k_cache) + off);
-        vst[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.v_cache) + off);
-      }
+      const int64_t off = base + static_cast<int64_t>((key + j) & bmask) * kHead;
+      kr[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.k_cache) + off);
+      vr[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.v_cache) + off);
     }
   };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&s_k[(sk + j) * kKRow + sc * 8]) = kst[j];
+  auto store = [&](int buf, const u32x4 (&kr)[2], const u32x4 (&vr)[2], int valid) {
+    T* sk_buf = s_k + buf * kTileK;
+    T* sv_buf = s_vt + buf * kTileV;
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    const u32x4 v0 = (valid & 1) ? vr[0] : z, v1 = (valid & 2) ? vr[1] : z;
+    *reinterpret_cast<u32x4*>(&sk_buf[sk * kKRow + sc * 8]) = kr[0];
+    *reinterpret_cast<u32x4*>(&sk_buf[(sk + 1) * kKRow + sc * 8]) = kr[1];
     // V transposed: dims sc * 8 .. + 7, keys sk and sk + 1 side by side.
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t a0 = vst[0][w], a1 = vst[1][w];
+      const uint32_t a0 = v0[w], a1 = v1[w];
       const int d = sc * 8 + 2 * w;
-      *reinterpret_cast<uint32_t*>(&s_vt[d * kVRow + sk]) = (a0 & 0xffffu) | (a1 << 16);
-      *reinterpret_cast<uint32_t*>(&s_vt[(d + 1) * kVRow + sk]) = (a0 >> 16) | (a1 & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(&sv_buf[d * kVRow + sk]) = (a0 & 0xffffu) | (a1 << 16);
+      *reinterpret_cast<uint32_t*>(&sv_buf[(d + 1) * kVRow + sk]) = (a0 >> 16) | (a1 & 0xffff0000u);
     }
   };
 
@@ -170,45 +187,48 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   float m_ref = -INFINITY;  // reference maximum of this lane's column (base 2)
   float l_part = 0.0f;      // sum of this lane's probabilities (its 16 keys of each tile)
 
-  load_tile(0);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int t0 = tile * kKeys;
-    __syncthreads();  // the previous tile's reads of the LDS tiles are done
-    store_tile();
-    __syncthreads();
-    if (tile + 1 < n_tiles) load_tile(t0 + kKeys);
-
+  auto compute = [&](int t, int buf) {
+    const T* sk_buf = s_k + buf * kTileK;
+    const T* sv_buf = s_vt + buf * kTileV;
+    const int t0 = t * kKeys;
     // S^T for 32 keys x this wave's 32 columns.
     f32x16 s = f32x16{};
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(&s_k[(lane % 32) * kKRow + 16 * sl + 8 * half]);
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(&sk_buf[(lane % 32) * kKRow + 16 * sl + 8 * half]);
       s = M::mma(ka, qb[sl], s);
     }
-
-    // Scores in base 2, masked; lane holds keys t0 + 8j + 4 half + i, j, i = 0..3.
-    float tmax = -INFINITY;
+    // Causal mask, only on tiles that reach past the wave's first position; lane holds
+    // keys t0 + 8j + 4 half + i, j, i = 0..3.  (Columns past the chunk have pos >= L and
+    // zero queries: they compute finite values that are never stored.)
+    if (t0 + kKeys - 1 > pos_min) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = t0 + 8 * (r / 4) + 4 * half + (r % 4);
-      const float z = (col_ok && key <= pos) ? s[r] * a.scale_log2 : -INFINITY;
-      s[r] = z;
-      tmax = fmaxf(tmax, z);
+      for (int r = 0; r < 16; ++r) {
+        const int key = t0 + 8 * (r / 4) + 4 * half + (r % 4);
+        s[r] = key <= pos ? s[r] : -INFINITY;
+      }
     }
+    // Maximum of the raw scores (the scale is positive, so it commutes), then base 2.
+    float tmax = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // the column's other 16 keys
-    if (tmax > m_ref + kRescaleSlack) {
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - tmax);  // 0 on the first tile
-      m_ref = tmax;
+    const float c = a.scale_log2;
+    const float tm = tmax * c;
+    if (tm > m_ref + kRescaleSlack) {
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - tm);  // 0 on the first tile
+      m_ref = tm;
       l_part *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
-    // Probabilities, split into a 16-bit value and the 16-bit rounding of the rest.
+    // Probabilities exp2(s c - m), split into a 16-bit value and the 16-bit rounding of
+    // the rest.
     uint32_t ph[8], pl[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = col_ok ? __builtin_amdgcn_exp2f(s[r] - m_ref) : 0.0f;
-      const float p1 = col_ok ? __builtin_amdgcn_exp2f(s[r + 1] - m_ref) : 0.0f;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_ref));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -m_ref));
       l_part += p0 + p1;
       const T h0 = static_cast<T>(p0), h1 = static_cast<T>(p1);
       const T e0 = static_cast<T>(p0 - static_cast<float>(h0));
@@ -225,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       const u32x4 bl = u32x4{pl[4 * q], pl[4 * q + 1], pl[4 * q + 2], pl[4 * q + 3]};
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const T* vrow = &s_vt[(32 * dt + lane % 32) * kVRow + 16 * q + 4 * half];
+        const T* vrow = &sv_buf[(32 * dt + lane % 32) * kVRow + 16 * q + 4 * half];
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
         const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
@@ -233,7 +253,46 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         o[dt] = M::mma(va, bl, o[dt]);
       }
     }
+  };
+
+  // Pipeline: tile t is computed from LDS while tile t + 1 waits in registers (to be
+  // stored into the other buffer) and tile t + 2's loads are in flight; block ids run
+  // one tile further ahead, issued before the data loads they precede.
+  u32x4 ka[2], va[2], kb[2], vb[2];
+  int ma, mb;
+  const int id0 = tile_block(0);
+  const int id1 = tile_block(1);
+  issue(0, id0, ka, va, ma);
+  int id_next = tile_block(2);
+  issue(1, id1, kb, vb, mb);
+  store(0, ka, va, ma);
+  __syncthreads();
+  // Drain the prologue's loads once: the loop header then sees only its own back edge's
+  // loads in flight, and its waits stay as loose as the pipeline allows.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // The scheduling barriers keep the phases in this order, so that the wait for a staged
+  // tile's loads sits at its store, after the compute, and not before the next loads.
+  // Pairs of tiles per trip with one exit test, so that the loop header is reached only
+  // from the prologue and from the end of a pair.
+  int id_a = id_next;  // block ids of tile t + 2 at the top of a pair
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    const int id3 = tile_block(t + 3);
+    issue(t + 2, id_a, ka, va, ma);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(t, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    store(1, kb, vb, mb);
+    __syncthreads();
+    id_a = tile_block(t + 4);
+    issue(t + 3, id3, kb, vb, mb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(t + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    store(0, ka, va, ma);
+    __syncthreads();
   }
+  if (t < n_tiles) compute(t, 0);  // an odd tile count: the last tile is in buffer 0
 
   // A block id outside the pool anywhere in the workgroup's keys makes every output NaN.
   bad_blk = __syncthreads_or(bad_blk);

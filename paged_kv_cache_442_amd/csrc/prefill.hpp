@@ -17,6 +17,7 @@ struct PrefillArgs {
   const int32_t* ctx;         // [S]
   float* out;                 // [num_rows][Hq][128]
   int32_t num_rows, num_seqs, num_q_heads, num_kv_heads, max_blocks, num_blocks, block_size;
+  int32_t block_shift;        // log2(block_size): block sizes are powers of two here
   int32_t max_context;
   float scale_log2;           // scale * log2(e)
 };

@@ -340,3 +340,89 @@ class PrefixCacheSession:
     def decode(self, requests, stream=None):
         """Decode the newest token of each request in ``requests``; returns ``out``."""
         return self.run_decode(self.decode_args(requests), stream)
+
+
+class SharedPrefixSession:
+    """Parallel sampling over a ``workloads.SharedPrefixWorkload``.
+
+    Each group's shared context is written once and forked into its branches; every
+    branch's first divergent token triggers copy-on-write (the reported pairs are
+    copied with ``pa_copy_blocks``), then the rest of each tail is appended and written.
+    ``decode`` runs ``pa_decode`` over all branches, whose tables share the groups'
+    full context blocks.
+    """
+
+    def __init__(self, w, device="cuda", poison=True):
+        self.w = w
+        self.device = device
+        self.desc = pa.make_desc(1, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype)
+        self.storage = torch.empty(pa.pa_pool_bytes(self.desc), dtype=torch.uint8, device=device)
+        if poison:
+            nan_fill(self.storage, w.dtype)
+        pool = self.pool = pa.pa_alloc_pool(self.desc, self.storage, w.free_order)
+
+        def write(k, v, slots):
+            pa.pa_reshape_and_cache(pool, 0, bits_to_device(k, w.dtype, device),
+                                    bits_to_device(v, w.dtype, device),
+                                    torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).to(device))
+
+        groups = []
+        for g in range(w.groups):
+            root = pa.pa_seq_new(pool)
+            a, b = w.shared_offsets[g], w.shared_offsets[g + 1]
+            write(w.shared_k[a:b], w.shared_v[a:b], pa.pa_seq_append(pool, root, b - a)[0])
+            groups.append([root] + [pa.pa_seq_fork(pool, root) for _ in range(w.branches - 1)])
+        self.seqs = sorted(s for grp in groups for s in grp)
+        self.branch_of = {s: g * w.branches + b for g, grp in enumerate(groups) for b, s in enumerate(grp)}
+        # First divergent token of every branch: copy-on-write pairs, then the copies.
+        pairs, first_slots, first_rows = [], [], []
+        for s in self.seqs:
+            slots, p = pa.pa_seq_append(pool, s, 1)
+            pairs += p
+            first_slots.append(slots[0])
+            first_rows.append(w.tail_offsets[self.branch_of[s]])
+        self.cow_pairs = pairs
+        self.pairs_dev = torch.tensor(pairs, dtype=torch.int32, device=device).reshape(-1, 2)
+        pa.pa_copy_blocks(pool, self.pairs_dev)
+        rows = np.array(first_rows)
+        write(w.tail_k[rows], w.tail_v[rows], first_slots)
+        for s in self.seqs:
+            i = self.branch_of[s]
+            a, e = w.tail_offsets[i] + 1, w.tail_offsets[i + 1]
+            if e > a:
+                slots, p = pa.pa_seq_append(pool, s, e - a)
+                if p:
+                    raise RuntimeError("a second copy-on-write in one branch")
+                write(w.tail_k[a:e], w.tail_v[a:e], slots)
+        self.lens = [pa.pa_seq_length(pool, s) for s in self.seqs]
+        self.max_blocks = max(-(-L // w.block_size) for L in self.lens)
+        tables, ctx = pa.pa_export_block_tables(pool, self.seqs, self.max_blocks)
+        self.tables_host = tables
+        self.tables = torch.from_numpy(tables).to(device)
+        self.ctx = torch.from_numpy(ctx).to(device)
+        order = [self.branch_of[s] for s in self.seqs]   # q row i belongs to branch i
+        self.q = bits_to_device(w.q[order], w.dtype, device)
+        self.max_context = max(self.lens)
+        self.out = torch.empty(len(self.seqs), w.num_q_heads, w.head_dim, dtype=torch.float32,
+                               device=device)
+        self.workspace = torch.empty(pa.pa_decode_workspace_bytes(pool, len(self.seqs), w.num_q_heads,
+                                                                  self.max_context, 0),
+                                     dtype=torch.uint8, device=device)
+        self.scale = 1.0 / math.sqrt(w.head_dim)
+
+    def copy_blocks(self, stream=None):
+        pa.pa_copy_blocks(self.pool, self.pairs_dev, stream)
+
+    def decode(self, stream=None):
+        pa.pa_decode(self.pool, 0, self.q, self.tables, self.ctx, self.max_context, self.scale,
+                     self.out, self.workspace, 0, stream)
+
+    def branch_tokens(self, s):
+        """(K, V) raw bits of branch sequence ``s``, in token order."""
+        w = self.w
+        i = self.branch_of[s]
+        g = i // w.branches
+        sk = slice(w.shared_offsets[g], w.shared_offsets[g + 1])
+        tk = slice(w.tail_offsets[i], w.tail_offsets[i + 1])
+        return (np.concatenate([w.shared_k[sk], w.tail_k[tk]]),
+                np.concatenate([w.shared_v[sk], w.tail_v[tk]]))
