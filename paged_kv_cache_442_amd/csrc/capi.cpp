@@ -131,7 +131,7 @@ int prepare_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs
   if (d.block_size % pa::kTileTokens != 0)
     return fail(PA_E_UNSUPPORTED, "block_size %d (must be a multiple of %d)", d.block_size,
                 pa::kTileTokens);
-  if (partition_tokens == 0) partition_tokens = pa::kDefaultPartition;
+  if (partition_tokens == 0) partition_tokens = pa::default_partition(group);
   if (partition_tokens < 0 || partition_tokens % (pa::kTileTokens * pa::kDecodeWaves) != 0 ||
       partition_tokens > pa::kMaxPartition)
     return fail(PA_E_INVAL, "partition_tokens %d must be a positive multiple of %d, at most %d",
@@ -487,7 +487,10 @@ int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t
   if (!pool) return fail(PA_E_INVAL, "pool is NULL");
   if (num_seqs < 0 || num_q_heads < 0 || max_context < 0 || partition_tokens < 0)
     return fail(PA_E_INVAL, "negative size");
-  if (partition_tokens == 0) partition_tokens = pa::kDefaultPartition;
+  if (partition_tokens == 0) {
+    const int32_t hkv = pool->desc.num_kv_heads;
+    partition_tokens = pa::default_partition(hkv > 0 ? num_q_heads / hkv : 1);
+  }
   const int64_t pmax =
       std::max<int64_t>(1, (static_cast<int64_t>(max_context) + partition_tokens - 1) / partition_tokens);
   // Partials are needed only when a sequence can span more than one partition.

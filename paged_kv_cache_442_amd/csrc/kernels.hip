@@ -25,6 +25,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // A score may exceed the running reference maximum by this much (base-2 units)
 // before the accumulators are rescaled: probabilities stay below 2^8, far from fp32
@@ -68,6 +70,11 @@ struct ElemF16 {
     return r;
   }
   __device__ static u32x4 k_operand(Chunk c) { return c; }
+  // 16 tokens x 16 heads of scores from 32 dims (A = K rows, B = query columns).
+  __device__ static f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
   __device__ static void widen(Chunk c, float (&v)[kElems]) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -94,6 +101,10 @@ struct ElemBF16 {
     return r;
   }
   __device__ static u32x4 k_operand(Chunk c) { return c; }
+  __device__ static f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
   __device__ static void widen(Chunk c, float (&v)[kElems]) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -112,6 +123,7 @@ struct ElemFP8 {
   static constexpr int kBytes = 1, kQBytes = 2, kElems = 8;
   __device__ static float dot(uint32_t q, uint32_t k, float acc) { return ElemBF16::dot(q, k, acc); }
   __device__ static float dot0(uint32_t q, uint32_t k) { return ElemBF16::dot0(q, k); }
+  __device__ static f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) { return ElemBF16::mma16(a, b, c); }
   template <bool HI>
   __device__ static uint32_t to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
@@ -164,9 +176,17 @@ template <class E, int GW>
 struct DecodeLds {
   static constexpr int NCH = kHeadDim / E::kElems;  // lane chunks per K/V row
   static constexpr int TG = kWave / NCH;            // rows per wave-wide load
-  float o[kDecodeWaves][TG][GW][kHeadDim];
+  // Each row of o is padded by 4 floats, and dims are stored permuted (see o_pos) so
+  // that the lanes of a row write 16 consecutive 16-byte pieces: no bank conflicts.
+  static constexpr int kRow = kHeadDim + 4;
+  float o[kDecodeWaves][GW][TG][kRow];
   float m[kDecodeWaves][GW];
   float l[kDecodeWaves][GW];
+  // Position of dims d .. d + 3 (d a multiple of 4) within a row: the piece (d % VD) / 4
+  // of every chunk first, chunks in order.
+  __device__ static constexpr int o_pos(int d) {
+    return ((d % E::kElems) / 4) * (4 * NCH) + (d / E::kElems) * 4;
+  }
 };
 
 // DPP controls (16-lane rows): partner lane a ^ 8, a ^ 7, a ^ 2, a ^ 1 and broadcast of
@@ -245,12 +265,17 @@ __device__ __forceinline__ void fma_row_bcast(float& acc, float p, float v) {
                : "v"(p), "v"(v), "i"(LANE));
 }
 
-template <int GW, int VD, int H>
+// Lane position (0..15) of the row that holds head h's probability: after the DPP
+// butterfly (GroupLayout), or lane h itself when the scores come from MFMA.
+template <int GW, bool MF>
+constexpr int prob_lane(int h) { return MF ? h : GroupLayout<GW>::lane_of_head(h); }
+
+template <int GW, int VD, int H, bool MF>
 __device__ __forceinline__ void pv_row(float (&o)[GW][VD], float pr, const float (&v)[VD]) {
   if constexpr (H < GW) {
 #pragma unroll
-    for (int e = 0; e < VD; ++e) fma_row_bcast<GroupLayout<GW>::lane_of_head(H)>(o[H][e], pr, v[e]);
-    pv_row<GW, VD, H + 1>(o, pr, v);
+    for (int e = 0; e < VD; ++e) fma_row_bcast<prob_lane<GW, MF>(H)>(o[H][e], pr, v[e]);
+    pv_row<GW, VD, H + 1, MF>(o, pr, v);
   }
 }
 
@@ -314,7 +339,9 @@ struct Unit {
 // carries (query and output registers), the fewer workgroups fit.
 template <class E, int GW>
 constexpr int decode_blocks_per_cu() {
-  return E::kBytes == 4 ? 2 : (GW >= 8 ? 2 : GW >= 4 ? 3 : 4);
+  // GW >= 4 with 16-bit queries runs the MFMA path, which keeps two tiles of K and V in
+  // flight per wave: two workgroups fit.
+  return E::kBytes == 4 ? 2 : (GW >= 4 ? 2 : 4);
 }
 
 template <class E, int GW, int HS>
@@ -330,6 +357,17 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
   constexpr int QDW = G * kHeadDim * E::kQBytes / 4;  // dwords of one group's query rows
   using Chunk = typename E::Chunk;
   constexpr int QPT = (QDW + kWave * kDecodeWaves - 1) / (kWave * kDecodeWaves);
+  // With 16-bit queries and groups of 4 or 8, QK runs on MFMA (16x16x32): the A operand
+  // is 16 tokens x 32 dims of K (lane l: token l % 16, dims 8 (l / 16) .. + 7 of the
+  // slice), the B operand 32 dims x 16 query heads (heads past G are zero), and the
+  // result gives lane l the scores of head l % 16 for tokens 4 (l / 16) + i, i = 0..3.
+  // V load i then reads tokens 4r + i into row r, so each row's probabilities sit in
+  // the row that holds the V values they weight, and PV is the same row-broadcast FMA.
+  constexpr bool MF = E::kQBytes == 2 && GW >= 4 && HS == 1;
+  static_assert(!MF || (NCH == 16 && LOADS == 4), "MFMA scores assume 16-lane rows, 4 loads");
+  // Tiles per step: the MFMA path has the registers to keep two tiles' K and V in flight.
+  constexpr int TS = MF ? 2 : 1;
+  constexpr int NL = TS * LOADS;  // K (and V) loads per step
   constexpr int64_t kRowBytes = kHeadDim * E::kBytes;
 
   __shared__ Lds lds;
@@ -343,7 +381,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
   const int half = wave / NS;    // takes query heads half * GW .. half * GW + GW - 1
   const int rr = lane / NCH;  // token row of the lane within each 1 KiB load
   const int ch = lane % NCH;  // 16-byte chunk of that row
-  const int hsel = GL::head_of_lane(lane & 15);
+  const int hsel = MF ? (lane & 15) : GL::head_of_lane(lane & 15);
   const int P = a.partition_tokens;
 
   auto unit_of = [&](int work) -> Unit {
@@ -417,8 +455,8 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     load_q(it, qd);
     stage_q(qd);
   }
-  bool prefetched = false;  // kr / vr already hold (or are receiving) the unit's tile 0
-  Chunk kr[LOADS], vr[LOADS];
+  bool prefetched = false;  // kr / vr already hold (or are receiving) the unit's step 0
+  Chunk kr[TS * LOADS], vr[TS * LOADS];
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
 
@@ -435,14 +473,21 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     const int t_end = t_end_of(it);
     const int t_lo = window_start(it.L, a.window);  // tokens before it are outside the window
 
-    u32x4 qv[GW];
+    u32x4 qv[MF ? 4 : GW];
     {
       // Recomputed per unit on purpose: hoisted out of the loop, the G addresses would
       // stay live through the tile loop and spill.
       int hs = hsel;
       asm volatile("" : "+v"(hs));
+      if constexpr (MF) {
+        // B operand of slice s: head hs, dims 32 s + 8 rr .. + 7 (chunk 4 s + rr).
 #pragma unroll
-      for (int p = 0; p < GW; ++p) qv[p] = s_q[(half * GW + GL::slot_head(hs, p)) * NCH + ch];
+        for (int k = 0; k < 4; ++k)
+          qv[k] = hs < G ? s_q[hs * NCH + 4 * k + rr] : u32x4{0u, 0u, 0u, 0u};
+      } else {
+#pragma unroll
+        for (int p = 0; p < GW; ++p) qv[p] = s_q[(half * GW + GL::slot_head(hs, p)) * NCH + ch];
+      }
     }
 
     // Tile n of the wave's stream: this unit's tiles, then (when the next unit has
@@ -453,15 +498,37 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     // A block id outside the pool (row offset -1) makes the unit's result NaN; such
     // tiles are read from block 0 instead, so nothing outside the pool is touched.
     const bool bad_blk = __builtin_amdgcn_ballot_w64(lane < nt && rows_cur < 0) != 0;
-    auto issue = [&](int n, const char* base, Chunk (&r)[LOADS]) {
-      int rows = (n >= nt && cross) ? __builtin_amdgcn_readlane(rows_next, 0)
-                                    : __builtin_amdgcn_readlane(rows_cur, min(n, nt - 1));
-      rows = max(rows, 0);
-      const Chunk* src = reinterpret_cast<const Chunk*>(base + static_cast<int64_t>(rows) * kRowBytes) + lane;
+    // Lane chunk offsets within the tile: K load i (MFMA: token ch, dim chunk 4 i + rr;
+    // else token 4 i + rr, chunk ch) and V load i (MFMA: token 4 rr + i, chunk ch).
+    const int k_off = MF ? ch * NCH + rr : lane;
+    const int v_off = MF ? 4 * rr * NCH + ch : lane;
+    constexpr int k_step = MF ? 4 : kWave;
+    constexpr int v_step = MF ? NCH : kWave;
+    // Step n covers the wave's tiles TS n .. TS n + TS - 1.  Past the unit's steps it
+    // fetches the next unit's first step (when the next unit has tiles on this wave),
+    // else this unit's last tile again (a cache hit), so every pass has the same loads
+    // in flight and the same waits; tiles past the wave's last one repeat the last
+    // tile's rows and are masked out by their tokens.
+    const int ns = (nt + TS - 1) / TS;
+    auto rows_of = [&](int n, int u) -> int {
+      const int rows = n >= ns ? (cross ? __builtin_amdgcn_readlane(rows_next, min(u, nt_nx - 1))
+                                        : __builtin_amdgcn_readlane(rows_cur, nt - 1))
+                               : __builtin_amdgcn_readlane(rows_cur, min(TS * n + u, nt - 1));
+      return max(rows, 0);
+    };
+    // K and V are read once per decode step: streaming loads keep them from displacing
+    // reusable lines (measured 3-6% faster than plain loads).
+    auto load_one = [&](const char* base, int rows, int off, int idx) -> Chunk {
+      const Chunk* src = reinterpret_cast<const Chunk*>(base + static_cast<int64_t>(rows) * kRowBytes) + off;
+      return __builtin_nontemporal_load(src + idx);
+    };
+    auto issue = [&](int n, const char* base, Chunk (&r)[NL], int off, int step) {
 #pragma unroll
-      // K and V are read once per decode step: streaming loads keep them from
-      // displacing reusable lines (measured 3-6% faster than plain loads).
-      for (int i = 0; i < LOADS; ++i) r[i] = __builtin_nontemporal_load(src + i * kWave);
+      for (int u = 0; u < TS; ++u) {
+        const int rows = rows_of(n, u);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) r[u * LOADS + i] = load_one(base, rows, off, i * step);
+      }
     };
 
     // The next unit's row offsets and query rows, loaded once this unit is under way.
@@ -474,8 +541,8 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     };
 
     if (nt > 0 && !prefetched) {
-      issue(0, kbase, kr);
-      issue(0, vbase, vr);
+      issue(0, kbase, kr, k_off, k_step);
+      issue(0, vbase, vr, v_off, v_step);
     }
 
     float o[GW][VD];
@@ -489,50 +556,74 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     // Tile n's K and V are in kr / vr on entry; tile n + 1's are on their way into the
     // same registers on exit, each issued as soon as tile n has consumed the registers.
     auto process = [&](int n) {
-      const int t0 = t_begin + (stream + NS * n) * kTileTokens;
-      // Partial dot products of every load first, then the butterflies of all loads
-      // level by level, so that no DPP step waits on the instruction just before it.
-      float s[LOADS][GW];
+      // First token of tile u of this step, and the token of a lane's value i in it
+      // (score i, and V load i's row).
+      auto tile_t0 = [&](int u) { return t_begin + (stream + NS * (TS * n + u)) * kTileTokens; };
+      auto token = [&](int u, int i) {
+        return MF ? tile_t0(u) + 4 * rr + i : tile_t0(u) + i * TG + rr;
+      };
+      float z[NL];
+      if constexpr (MF) {
+        f32x4 acc[TS];
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const u32x4 kk = E::k_operand(kr[i]);
+        for (int u = 0; u < TS; ++u) {
+          acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int p = 0; p < GW; ++p) {
-          float acc = E::dot0(qv[p].x, kk.x);
-          acc = E::dot(qv[p].y, kk.y, acc);
-          acc = E::dot(qv[p].z, kk.z, acc);
-          s[i][p] = E::dot(qv[p].w, kk.w, acc);
+          for (int k = 0; k < 4; ++k) acc[u] = E::mma16(E::k_operand(kr[u * LOADS + k]), qv[k], acc[u]);
         }
-      }
-      if (n == 0) load_next();
-      issue(n + 1, kbase, kr);
-      if constexpr (NCH == 32) {
-        // A row spans two DPP rows: add the other half of the row first.
+        if (n == 0) load_next();
+        issue(n + 1, kbase, kr, k_off, k_step);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i)
+        for (int u = 0; u < TS; ++u)
 #pragma unroll
-          for (int p = 0; p < GW; ++p) s[i][p] += __shfl_xor(s[i][p], 16);
-      }
-      row_butterfly<GW, LOADS>(s);
-      float z[LOADS];
+          for (int i = 0; i < LOADS; ++i) {
+            const int t = token(u, i);
+            z[u * LOADS + i] = (t < t_end && t >= t_lo) ? acc[u][i] * a.scale_log2 : -INFINITY;
+          }
+      } else {
+        // Partial dot products of every load first, then the butterflies of all loads
+        // level by level, so that no DPP step waits on the instruction just before it.
+        float s[LOADS][GW];
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        pin(s[i][0]);
-        const int t = t0 + i * TG + rr;
-        z[i] = (t < t_end && t >= t_lo) ? s[i][0] * a.scale_log2 : -INFINITY;
+        for (int i = 0; i < LOADS; ++i) {
+          const u32x4 kk = E::k_operand(kr[i]);
+#pragma unroll
+          for (int p = 0; p < GW; ++p) {
+            float acc = E::dot0(qv[p].x, kk.x);
+            acc = E::dot(qv[p].y, kk.y, acc);
+            acc = E::dot(qv[p].z, kk.z, acc);
+            s[i][p] = E::dot(qv[p].w, kk.w, acc);
+          }
+        }
+        if (n == 0) load_next();
+        issue(n + 1, kbase, kr, k_off, k_step);
+        if constexpr (NCH == 32) {
+          // A row spans two DPP rows: add the other half of the row first.
+#pragma unroll
+          for (int i = 0; i < LOADS; ++i)
+#pragma unroll
+            for (int p = 0; p < GW; ++p) s[i][p] += __shfl_xor(s[i][p], 16);
+        }
+        row_butterfly<GW, LOADS>(s);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          pin(s[i][0]);
+          const int t = token(0, i);
+          z[i] = (t < t_end && t >= t_lo) ? s[i][0] * a.scale_log2 : -INFINITY;
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
 
       bool over = false;
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) over |= z[i] > m_ref + kRescaleSlack;
+      for (int i = 0; i < NL; ++i) over |= z[i] > m_ref + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(over) != 0) {
         // Raise each head's reference maximum to the tile's maximum and rescale.  Lanes
         // of one head within a row hold the same scores; rows of other tokens are other
         // lanes 16 (or 32) apart.
         float tmax = z[0];
 #pragma unroll
-        for (int i = 1; i < LOADS; ++i) tmax = fmaxf(tmax, z[i]);
+        for (int i = 1; i < NL; ++i) tmax = fmaxf(tmax, z[i]);
 #pragma unroll
         for (int m = NCH; m < kWave; m <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, m));
         const float m_new = fmaxf(m_ref, tmax);
@@ -542,49 +633,55 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
 #pragma unroll
         for (int h = 0; h < GW; ++h) {
           const float ah =
-              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), GL::lane_of_head(h)));
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), prob_lane<GW, MF>(h)));
 #pragma unroll
           for (int e = 0; e < VD; ++e) o[h][e] *= ah;
         }
       }
 
-      const bool partial_tile = t0 + kTileTokens > t_end || t0 < t_lo;
+      // Each V register is reloaded with the next step's value as soon as PV has used
+      // it, so the next step's V loads leave during this step's PV rather than after it.
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const float pr = __builtin_amdgcn_exp2f(z[i] - m_ref);
-        l_acc += pr;
-        float v[VD];
-        E::widen(vr[i], v);
-        if (partial_tile) {
-          // Rows past the context (or before the window) may hold anything, even NaN:
-          // drop them by select.
-          const bool keep = t0 + i * TG + rr < t_end && t0 + i * TG + rr >= t_lo;
+      for (int u = 0; u < TS; ++u) {
+        const bool partial_tile = tile_t0(u) + kTileTokens > t_end || tile_t0(u) < t_lo;
+        const int vrows = rows_of(n + 1, u);
 #pragma unroll
-          for (int e = 0; e < VD; ++e) {
-            pin(v[e]);
-            v[e] = keep ? v[e] : 0.0f;
+        for (int i = 0; i < LOADS; ++i) {
+          const float pr = __builtin_amdgcn_exp2f(z[u * LOADS + i] - m_ref);
+          l_acc += pr;
+          float v[VD];
+          E::widen(vr[u * LOADS + i], v);
+          if (partial_tile) {
+            // Rows past the context (or before the window) may hold anything, even NaN:
+            // drop them by select.
+            const bool keep = token(u, i) < t_end && token(u, i) >= t_lo;
+#pragma unroll
+            for (int e = 0; e < VD; ++e) {
+              pin(v[e]);
+              v[e] = keep ? v[e] : 0.0f;
+            }
           }
-        }
-        if constexpr (GW == 1) {
+          if constexpr (GW == 1) {
 #pragma unroll
-          for (int e = 0; e < VD; ++e) o[0][e] = fmaf(pr, v[e], o[0][e]);
-        } else {
-          // o[h] += p(head h, this row) * v: the probability comes straight from the
-          // lane holding head h through the FMA's row broadcast.  Two wait states
-          // separate the write of pr from its first DPP read.
-          // (pr is an operand of the s_nop so that its computation cannot be scheduled
-          // between the s_nop and the FMAs.)
-          asm volatile("s_nop 1" ::"v"(pr));
-          pv_row<GW, VD, 0>(o, pr, v);
+            for (int e = 0; e < VD; ++e) o[0][e] = fmaf(pr, v[e], o[0][e]);
+          } else {
+            // o[h] += p(head h, this row) * v: the probability comes straight from the
+            // lane holding head h through the FMA's row broadcast.  Two wait states
+            // separate the write of pr from its first DPP read.
+            // (pr is an operand of the s_nop so that its computation cannot be scheduled
+            // between the s_nop and the FMAs.)
+            asm volatile("s_nop 1" ::"v"(pr));
+            pv_row<GW, VD, 0, MF>(o, pr, v);
+          }
+          vr[u * LOADS + i] = load_one(vbase, vrows, v_off, i * v_step);
+          // One load's probabilities and V values at a time: interleaving the loads
+          // would keep all of them live and spill.
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // One load's probabilities and V values at a time: interleaving the loads
-        // would keep all of them live and spill.
-        __builtin_amdgcn_sched_barrier(0);
       }
-      issue(n + 1, vbase, vr);
     };
 
-    for (int n = 0; n < nt; ++n) process(n);
+    for (int n = 0; n < ns; ++n) process(n);
     if (!next_loaded) load_next();
     prefetched = nt > 0 && cross;
 
@@ -603,9 +700,9 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
 #pragma unroll
         for (int r = 0; r < TG; ++r)
           sum += __int_as_float(
-              __builtin_amdgcn_readlane(__float_as_int(l_acc), r * NCH + GL::lane_of_head(h)));
+              __builtin_amdgcn_readlane(__float_as_int(l_acc), r * NCH + prob_lane<GW, MF>(h)));
         const float mh =
-            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_ref), GL::lane_of_head(h)));
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_ref), prob_lane<GW, MF>(h)));
         if (lane == 0) {
           lds.m[wave][h] = mh;
           lds.l[wave][h] = sum;
@@ -615,7 +712,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
       for (int h = 0; h < GW; ++h)
 #pragma unroll
         for (int e4 = 0; e4 < VD; e4 += 4)
-          *reinterpret_cast<f32x4*>(&lds.o[wave][rr][h][ch * VD + e4]) =
+          *reinterpret_cast<f32x4*>(&lds.o[wave][h][rr][Lds::o_pos(ch * VD + e4)]) =
               f32x4{o[h][e4], o[h][e4 + 1], o[h][e4 + 2], o[h][e4 + 3]};
       __syncthreads();
 
@@ -635,9 +732,10 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
           const int w = w0 + j;
           const float W = __builtin_amdgcn_exp2f(lds.m[w][hw] - M);
           lt += W * lds.l[w][hw];
-          f32x4 sum = *reinterpret_cast<const f32x4*>(&lds.o[w][0][hw][d4]);
+          const int pos = Lds::o_pos(d4);
+          f32x4 sum = *reinterpret_cast<const f32x4*>(&lds.o[w][hw][0][pos]);
 #pragma unroll
-          for (int r = 1; r < TG; ++r) sum += *reinterpret_cast<const f32x4*>(&lds.o[w][r][hw][d4]);
+          for (int r = 1; r < TG; ++r) sum += *reinterpret_cast<const f32x4*>(&lds.o[w][hw][r][pos]);
           acc += W * sum;
         }
         const f32x4 res = acc / lt * a.v_scale;

@@ -12,7 +12,10 @@ namespace pa {
 constexpr int kHeadDim = 128;        // head_dim the attention kernels are built for
 constexpr int kTileTokens = 16;      // tokens per K/V tile streamed by the decode kernel
 constexpr int kDecodeWaves = 4;      // waves per decode workgroup
-constexpr int kDefaultPartition = 512;
+// Default partition: groups of 4 or 8 query heads run the MFMA score path, whose units
+// carry a fixed end-of-unit merge that longer partitions amortize (measured 1024 best
+// for them); smaller groups balance better with 512.
+constexpr int default_partition(int group) { return group >= 4 ? 1024 : 512; }
 constexpr int kPlanThreads = 1024;
 // A wave's tiles of one unit must fit one wave of lanes; a workgroup has at least two
 // tile streams (four waves, at most two head halves).
