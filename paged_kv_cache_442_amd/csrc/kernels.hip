@@ -34,7 +34,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr float kRescaleSlack = 8.0f;
 
 // s_waitcnt immediate for "vmcnt(0)" with expcnt and lgkmcnt left at their maxima.
-constexpr int kWaitVmcnt0 = 0x0F70;
 
 // ------------------------------------------------------------------ element formats
 // Each format says how a lane's chunk of a K/V row is loaded (Chunk: the lane's kElems

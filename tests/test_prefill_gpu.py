@@ -142,3 +142,18 @@ def test_fp32_cache_is_rejected():
                               torch.ones(1, dtype=torch.int32, device="cuda"), 1, 1,
                               1 / math.sqrt(128), torch.zeros_like(q))
     assert e.value.code == pa.PA_E_UNSUPPORTED
+
+
+def test_block_size_that_is_not_a_power_of_two_is_rejected():
+    announce("prefill on a block size of 48 -> unsupported")
+    desc = pa.make_desc(1, 4, 48, 2, 128, pa.BF16)
+    storage = torch.zeros(pa.pa_pool_bytes(desc), dtype=torch.uint8, device="cuda")
+    pool = pa.pa_alloc_pool(desc, storage)
+    q = torch.zeros(1, 2, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_prefill_chunked(pool, 0, q, torch.tensor([0, 1], dtype=torch.int32, device="cuda"),
+                              torch.zeros(1, 1, dtype=torch.int32, device="cuda"),
+                              torch.ones(1, dtype=torch.int32, device="cuda"), 1, 1,
+                              1 / math.sqrt(128), torch.zeros(1, 2, 128, dtype=torch.float32,
+                                                              device="cuda"))
+    assert e.value.code == pa.PA_E_UNSUPPORTED
