@@ -66,8 +66,9 @@ _SIGNATURES = {
     "pa_decode_plan": (ctypes.c_int, _DECODE_ARGS),
     "pa_decode_partitions": (ctypes.c_int, _DECODE_ARGS),
     "pa_decode_reduce": (ctypes.c_int, _DECODE_ARGS),
+    "pa_prefill_workspace_bytes": (_I64, [_P, _I32, _I32, _I32]),
     "pa_prefill_chunked": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _I32,
-                                          _I32, ctypes.c_float, _P, _P]),
+                                          _I32, ctypes.c_float, _P, _P, _I64, _P]),
     "pa_decode_window": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _I32,
                                         ctypes.c_float, _I32, _P, _P, _I64, _P]),
     "pa_seq_release_before": (ctypes.c_int, [_P, _I32, _I32, _PI32]),
@@ -477,20 +478,27 @@ def pa_decode_reduce(pool, layer, q, block_tables, context_lens, max_context, sc
             scale, out, workspace, partition_tokens, stream)
 
 
+def pa_prefill_workspace_bytes(pool, num_rows, num_q_heads, max_context):
+    return _check(lib().pa_prefill_workspace_bytes(pool.handle, num_rows, num_q_heads, max_context))
+
+
 def pa_prefill_chunked(pool, layer, q, query_start, block_tables, context_lens, max_context,
-                       max_query_len, scale, out, stream=None):
+                       max_query_len, scale, out, workspace=None, stream=None):
     """q: GPU ``[R][H_q][d]`` pool dtype; query_start: GPU int32 ``[S+1]``; out: GPU fp32
-    ``[R][H_q][d]``."""
+    ``[R][H_q][d]``; workspace: GPU uint8 tensor of ``pa_prefill_workspace_bytes`` bytes
+    (None when that is 0)."""
     import torch
     R, H_q = q.shape[0], q.shape[1]
     S = query_start.numel() - 1
+    ws, ws_bytes = (None, 0) if workspace is None else \
+        (_dev(workspace, torch.uint8, "workspace"), workspace.numel())
     _check(lib().pa_prefill_chunked(pool.handle, layer, _dev(q, torch_dtype(pool.desc.kv_dtype), "q"),
                                     R, H_q, _dev(query_start, torch.int32, "query_start"), S,
                                     _dev(block_tables, torch.int32, "block_tables"),
                                     block_tables.shape[1],
                                     _dev(context_lens, torch.int32, "context_lens"), max_context,
                                     max_query_len, float(scale), _dev(out, torch.float32, "out"),
-                                    _stream(stream)))
+                                    ws, ws_bytes, _stream(stream)))
 
 
 def pa_decode_window(pool, layer, q, block_tables, context_lens, max_context, window, scale, out,

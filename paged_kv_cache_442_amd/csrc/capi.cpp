@@ -563,11 +563,28 @@ int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs, int
                           workspace_bytes, stream);
 }
 
+static int64_t prefill_pmax(int32_t max_context) {
+  return std::max<int64_t>(1, (static_cast<int64_t>(max_context) + pa::kPrefillPartKeys - 1) /
+                                  pa::kPrefillPartKeys);
+}
+
+int64_t pa_prefill_workspace_bytes(const pa_pool* pool, int32_t num_rows, int32_t num_q_heads,
+                                   int32_t max_context) {
+  if (!pool) return fail(PA_E_INVAL, "pool is NULL");
+  if (num_rows < 0 || num_q_heads < 0 || max_context < 0) return fail(PA_E_INVAL, "negative size");
+  const int64_t pmax = prefill_pmax(max_context);
+  if (pmax == 1) return 0;
+  const __int128 items = static_cast<__int128>(num_rows) * num_q_heads * pmax;
+  const __int128 bytes = items * pa::kHeadDim * 4 + ((items * 4 + 255) / 256) * 256;
+  if (bytes > std::numeric_limits<int64_t>::max() / 2) return fail(PA_E_RANGE, "workspace too large");
+  return static_cast<int64_t>(bytes);
+}
+
 int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_rows,
                        int32_t num_q_heads, const int32_t* query_start, int32_t num_seqs,
                        const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
                        int32_t max_context, int32_t max_query_len, float scale, float* out,
-                       void* stream) {
+                       void* workspace, int64_t workspace_bytes, void* stream) {
   int st = check_device_pool(pool, layer);
   if (st) return st;
   const pa_pool_desc& d = pool->desc;
@@ -617,9 +634,27 @@ int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_
   a.block_shift = __builtin_ctz(static_cast<unsigned>(d.block_size));
   a.max_context = max_context;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return hip_status(pa::launch_prefill(a, static_cast<int>(d.kv_dtype), group, max_query_len,
-                                       static_cast<hipStream_t>(stream)),
-                    "pa_prefill_chunked");
+  a.part_keys = pa::kPrefillPartKeys;
+  a.pmax = static_cast<int32_t>(prefill_pmax(max_context));
+  a.part_o = nullptr;
+  a.part_lse = nullptr;
+  if (a.pmax > 1) {
+    const int64_t need = pa_prefill_workspace_bytes(pool, num_rows, num_q_heads, max_context);
+    if (need < 0) return static_cast<int>(need);
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_E_INVAL, "workspace of %lld bytes < %lld needed (pa_prefill_workspace_bytes)",
+                  static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(PA_E_INVAL, "workspace must be 256-byte aligned");
+    const int64_t items = static_cast<int64_t>(num_rows) * num_q_heads * a.pmax;
+    a.part_lse = static_cast<float*>(workspace);
+    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((items * 4 + 255) / 256) * 256);
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(pa::launch_prefill(a, static_cast<int>(d.kv_dtype), group, max_query_len, s),
+                  "pa_prefill_chunked");
+  if (st) return st;
+  return hip_status(pa::launch_prefill_merge(a, group, max_query_len, s), "pa_prefill_chunked (merge)");
 }
 
 int pa_decode_window(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,

@@ -88,9 +88,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int half = lane / 32;  // which 8 of a 16-dim slice, which 4 keys of 8
   const int seq = blockIdx.y;
   const int kvh = blockIdx.z;
-  // Row blocks go last to first: a chunk's last rows see the most keys, so the longest
-  // workgroups start first.
-  const int r0 = (gridDim.x - 1 - blockIdx.x) * TR;
+  // blockIdx.x = (row block, part).  Row blocks go last to first: a chunk's last rows see
+  // the most keys, so the longest workgroups start first.
+  const int part = blockIdx.x % a.pmax;
+  const int r0 = (gridDim.x / a.pmax - 1 - blockIdx.x / a.pmax) * TR;
 
   const int qs = a.query_start[seq];
   const int n_rows = a.query_start[seq + 1] - qs;
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int64_t out_row = (static_cast<int64_t>(qs) + row) * a.num_q_heads + kvh * G + hh;
 
   if (bad) {
-    if (col_ok && !(qs < 0 || qs + n_rows > a.num_rows)) {
+    if (part == 0 && col_ok && !(qs < 0 || qs + n_rows > a.num_rows)) {
 #pragma unroll
       for (int d4 = 0; d4 < kHead; d4 += 8)
         *reinterpret_cast<f32x4*>(a.out + out_row * kHead + d4 + 4 * half) =
@@ -130,9 +131,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     for (int s = 0; s < 8; ++s) qb[s] = col_ok ? qrow[2 * s + half] : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // Largest key any column of the workgroup sees.
+  // Largest key any column of the workgroup sees, and this part's tiles of 0 .. kmax.
   const int kmax = L - n_rows + min(r0 + TR, n_rows) - 1;
-  const int n_tiles = kmax / kKeys + 1;
+  const int n_parts = kmax / a.part_keys + 1;
+  if (part >= n_parts) return;  // wave-uniform: the whole workgroup leaves
+  const int t_first = part * (a.part_keys / kKeys);
+  const int n_tiles = min(kmax, (part + 1) * a.part_keys - 1) / kKeys - t_first + 1;
 
   // Staging: thread t moves 16-byte chunk t / 16 of keys 2 (t % 16) and 2 (t % 16) + 1
   // (one block: block sizes are powers of two >= 16).  The 16 threads of a chunk hold 16
@@ -223,12 +227,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
     // Probabilities exp2(s c - m), split into a 16-bit value and the 16-bit rounding of
-    // the rest.
+    // the rest.  A column that has seen no key yet (possible in a later part of a split
+    // range) keeps m = -inf: its masked scores must give 0, not -inf - -inf.
+    const float mr = m_ref == -INFINITY ? 0.0f : m_ref;
     uint32_t ph[8], pl[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_ref));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -m_ref));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -mr));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -mr));
       l_part += p0 + p1;
       const T h0 = static_cast<T>(p0), h1 = static_cast<T>(p1);
       const T e0 = static_cast<T>(p0 - static_cast<float>(h0));
@@ -260,11 +266,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // one tile further ahead, issued before the data loads they precede.
   u32x4 ka[2], va[2], kb[2], vb[2];
   int ma, mb;
-  const int id0 = tile_block(0);
-  const int id1 = tile_block(1);
-  issue(0, id0, ka, va, ma);
-  int id_next = tile_block(2);
-  issue(1, id1, kb, vb, mb);
+  // Tile numbers below are relative to the part's first tile.
+  const int id0 = tile_block(t_first);
+  const int id1 = tile_block(t_first + 1);
+  issue(t_first, id0, ka, va, ma);
+  int id_next = tile_block(t_first + 2);
+  issue(t_first + 1, id1, kb, vb, mb);
   store(0, ka, va, ma);
   __syncthreads();
   // Drain the prologue's loads once: the loop header then sees only its own back edge's
@@ -277,36 +284,93 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   int id_a = id_next;  // block ids of tile t + 2 at the top of a pair
   int t = 0;
   for (; t + 1 < n_tiles; t += 2) {
-    const int id3 = tile_block(t + 3);
-    issue(t + 2, id_a, ka, va, ma);
+    const int id3 = tile_block(t_first + t + 3);
+    issue(t_first + t + 2, id_a, ka, va, ma);
     __builtin_amdgcn_sched_barrier(0);
-    compute(t, 0);
+    compute(t_first + t, 0);
     __builtin_amdgcn_sched_barrier(0);
     store(1, kb, vb, mb);
     __syncthreads();
-    id_a = tile_block(t + 4);
-    issue(t + 3, id3, kb, vb, mb);
+    id_a = tile_block(t_first + t + 4);
+    issue(t_first + t + 3, id3, kb, vb, mb);
     __builtin_amdgcn_sched_barrier(0);
-    compute(t + 1, 1);
+    compute(t_first + t + 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     store(0, ka, va, ma);
     __syncthreads();
   }
-  if (t < n_tiles) compute(t, 0);  // an odd tile count: the last tile is in buffer 0
+  if (t < n_tiles) compute(t_first + t, 0);  // an odd tile count: the last tile is in buffer 0
 
   // A block id outside the pool anywhere in the workgroup's keys makes every output NaN.
   bad_blk = __syncthreads_or(bad_blk);
   if (!col_ok) return;
   const float l_col = l_part + __shfl_xor(l_part, 32);
-  const float inv = bad_blk ? __builtin_nanf("") : 1.0f / l_col;
+  // A column may see no key of a later part (its row ends before the part): it then
+  // weighs nothing in the merge (lse -inf, o 0).
+  const float inv = bad_blk ? __builtin_nanf("") : (l_col > 0.0f ? 1.0f / l_col : 0.0f);
+  float* dst = a.out + out_row * kHead;
+  if (n_parts > 1) {
+    const int64_t prow = out_row * a.pmax + part;
+    dst = a.part_o + prow * kHead;
+    if (half == 0)
+      a.part_lse[prow] = bad_blk ? __builtin_nanf("") : (l_col > 0.0f ? m_ref + __log2f(l_col) : -INFINITY);
+  }
   // Lane holds dims 32 dt + 8 j + 4 half + i of its column.
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const f32x4 v = f32x4{o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2], o[dt][4 * j + 3]} * inv;
-      *reinterpret_cast<f32x4*>(a.out + out_row * kHead + 32 * dt + 8 * j + 4 * half) = v;
+      *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * j + 4 * half) = v;
     }
+}
+
+// Log-sum-exp merge of a row block's parts, for row blocks with more than one: the same
+// (row block, sequence, KV head) grid, one thread per (column, 4 dims) item in turn.
+//   M = max_p lse_p,  w_p = 2^(lse_p - M),  out = sum_p w_p o_p / sum_p w_p
+// (the identity of the softmax over a union of key sets; o_p is part p's normalized
+// output, lse_p its base-2 log-sum-exp).  A NaN in any part makes the output NaN.
+template <int G>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a) {
+  constexpr int TR = kCols / G;
+  const int seq = blockIdx.y;
+  const int kvh = blockIdx.z;
+  const int r0 = blockIdx.x * TR;
+  const int qs = a.query_start[seq];
+  const int n_rows = a.query_start[seq + 1] - qs;
+  if (r0 >= n_rows) return;
+  const int L = a.ctx[seq];
+  const bool bad = L < 0 || L > a.max_context ||
+                   static_cast<int64_t>(L) > static_cast<int64_t>(a.max_blocks) * a.block_size ||
+                   n_rows > L || qs < 0 || qs + n_rows > a.num_rows;
+  if (bad) return;  // the prefill kernel wrote its NaNs straight to out
+  const int kmax = L - n_rows + min(r0 + TR, n_rows) - 1;
+  const int n_parts = kmax / a.part_keys + 1;
+  if (n_parts == 1) return;
+  for (int item = threadIdx.x; item < kCols * (kHead / 4); item += blockDim.x) {
+    const int col = item / (kHead / 4);
+    const int d4 = (item % (kHead / 4)) * 4;
+    const int row = r0 + col % TR;
+    if (row >= n_rows) continue;
+    const int64_t out_row = (static_cast<int64_t>(qs) + row) * a.num_q_heads + kvh * G + col / TR;
+    const float* lse = a.part_lse + out_row * a.pmax;
+    float M = -INFINITY;
+    bool has_nan = false;
+    for (int p = 0; p < n_parts; ++p) {
+      has_nan |= lse[p] != lse[p];
+      M = fmaxf(M, lse[p]);
+    }
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float wsum = 0.0f;
+    for (int p = 0; p < n_parts; ++p) {
+      const float w = __builtin_amdgcn_exp2f(lse[p] - M);
+      wsum += w;
+      acc += w * *reinterpret_cast<const f32x4*>(a.part_o + (out_row * a.pmax + p) * kHead + d4);
+    }
+    const float nan = __builtin_nanf("");
+    *reinterpret_cast<f32x4*>(a.out + out_row * kHead + d4) =
+        has_nan ? f32x4{nan, nan, nan, nan} : acc / wsum;
+  }
 }
 
 template <class M>
@@ -327,7 +391,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int dtype, int group, int max_qu
                           hipStream_t s) {
   (void)hipGetLastError();
   const int tr = kCols / group;
-  const dim3 grid(static_cast<unsigned>((max_query_len + tr - 1) / tr),
+  const dim3 grid(static_cast<unsigned>((max_query_len + tr - 1) / tr * a.pmax),
                   static_cast<unsigned>(a.num_seqs), static_cast<unsigned>(a.num_kv_heads));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   switch (dtype) {
@@ -335,6 +399,23 @@ hipError_t launch_prefill(const PrefillArgs& a, int dtype, int group, int max_qu
     case 2: return launch_typed<MmaBF16>(a, group, grid, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_prefill_merge(const PrefillArgs& a, int group, int max_query_len, hipStream_t s) {
+  (void)hipGetLastError();
+  if (a.pmax <= 1) return hipSuccess;
+  const int tr = kCols / group;
+  const dim3 grid(static_cast<unsigned>((max_query_len + tr - 1) / tr),
+                  static_cast<unsigned>(a.num_seqs), static_cast<unsigned>(a.num_kv_heads));
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  switch (group) {
+    case 1: hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_merge_kernel<1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_merge_kernel<2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_merge_kernel<4>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(HIP_KERNEL_NAME(prefill_merge_kernel<8>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace pa

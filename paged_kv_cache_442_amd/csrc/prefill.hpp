@@ -20,11 +20,24 @@ struct PrefillArgs {
   int32_t block_shift;        // log2(block_size): block sizes are powers of two here
   int32_t max_context;
   float scale_log2;           // scale * log2(e)
+  // Split of long key ranges: a row block's keys go in parts of part_keys (a multiple of
+  // the 32-key tile); with more than one part each part writes its normalized output and
+  // base-2 log-sum-exp here, and the merge kernel combines them into `out`.
+  int32_t part_keys, pmax;
+  float* part_o;              // [num_rows][Hq][pmax][128]
+  float* part_lse;            // [num_rows][Hq][pmax]
 };
+
+// Keys per part of the split (64 tiles): long enough to amortize a part's start, short
+// enough that no single workgroup outlasts the batch.
+constexpr int kPrefillPartKeys = 2048;
 
 // dtype: 1 fp16, 2 bf16; group = num_q_heads / num_kv_heads in {1, 2, 4, 8}.  The grid
 // covers max_query_len rows of every sequence.
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int group, int max_query_len,
                           hipStream_t s);
+// Combines the parts of every row block that has more than one (nothing to do when
+// pmax == 1); launched after launch_prefill on the same stream.
+hipError_t launch_prefill_merge(const PrefillArgs& a, int group, int max_query_len, hipStream_t s);
 
 }  // namespace pa

@@ -226,6 +226,8 @@ class PrefillSession:
         self.q_c = bits_to_device(w.q_chunks, w.dtype, device)
         self.out_c = torch.empty(int(qs[-1]), w.num_q_heads, w.head_dim, dtype=torch.float32,
                                  device=device)
+        pws = pa.pa_prefill_workspace_bytes(self.pool, int(qs[-1]), w.num_q_heads, self.max_ctx_c)
+        self.workspace_c = torch.empty(pws, dtype=torch.uint8, device=device) if pws else None
         td, cd = tables_of(dec_seqs) if dec_seqs else (np.zeros((0, 1), np.int32), np.zeros(0, np.int32))
         self.tables_d_host, self.ctx_d_host = td, cd
         self.tables_d = torch.from_numpy(td).to(device)
@@ -244,7 +246,8 @@ class PrefillSession:
 
     def prefill(self, stream=None):
         pa.pa_prefill_chunked(self.pool, 0, self.q_c, self.query_start, self.tables_c, self.ctx_c,
-                              self.max_ctx_c, self.max_query_len, self.scale, self.out_c, stream)
+                              self.max_ctx_c, self.max_query_len, self.scale, self.out_c,
+                              self.workspace_c, stream)
 
     def decode(self, stream=None):
         if self.n_decode:

@@ -239,3 +239,12 @@ def test_batch_append_is_all_or_nothing():
     assert ei.value.code == pa.PA_E_INVAL
     slots, pairs = pa.pa_seq_append_batch(p, [b, a])
     assert len(slots) == 2 and pairs == []
+
+
+def test_prefill_workspace_is_needed_only_past_one_part():
+    pool = host_pool(8, 16)
+    assert pa.pa_prefill_workspace_bytes(pool, 100, 4, 2048) == 0
+    rows, heads, pmax = 100, 4, 3                      # 4097 keys: parts of 2048
+    items = rows * heads * pmax
+    lse = -(-items * 4 // 256) * 256
+    assert pa.pa_prefill_workspace_bytes(pool, rows, heads, 4097) == lse + items * 128 * 4

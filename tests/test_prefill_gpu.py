@@ -73,6 +73,20 @@ def test_prefill_small_shapes_all_rows(dtype, H_q, H_kv, bs):
     check_chunks(sess, lambda i: range(int(w.chunk_lens[i])))
 
 
+@pytest.mark.parametrize("dtype,H_q,H_kv", [(wl.BF16, 32, 8), (wl.F16, 64, 8), (wl.BF16, 8, 8)])
+def test_prefill_split_into_parts_all_rows(dtype, H_q, H_kv):
+    """Contexts past 2048 keys are split into parts and merged; a chunk across position
+    2048 has rows that see no key of the second part."""
+    announce(f"prefill split parts dtype={dtype} H_q={H_q} H_kv={H_kv}")
+    w = wl.custom_chunked(300 + H_q, dtype, [2000, 2100, 4000, 1], [100, 40, 65, 30], [], H_q, H_kv,
+                          block_size=16)
+    sess = PrefillSession(w)
+    assert sess.workspace_c is not None
+    sess.step()
+    torch.cuda.synchronize()
+    check_chunks(sess, lambda i: range(int(w.chunk_lens[i])))
+
+
 def test_prefill_single_rows_equal_the_decode_oracle():
     """A one-row chunk is a decode row: the same numbers as the oracle's decode."""
     announce("prefill with one-row chunks")
@@ -122,7 +136,7 @@ def test_invalid_sequences_get_nan_and_nothing_else_changes():
     ctx[1] = 10                            # 20 query rows but only 10 tokens
     out = torch.full_like(sess.out_c, 5.0)
     pa.pa_prefill_chunked(sess.pool, 0, sess.q_c, sess.query_start, tables, ctx, sess.max_ctx_c,
-                          sess.max_query_len, sess.scale, out)
+                          sess.max_query_len, sess.scale, out, sess.workspace_c)
     torch.cuda.synchronize()
     qs = sess.query_start.cpu().numpy()
     assert torch.isnan(out[qs[0]:qs[1]]).all()
