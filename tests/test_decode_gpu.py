@@ -211,3 +211,16 @@ def test_shared_prefix_copy_on_write_end_to_end():
                                            fpbits.decode(w.dtype, vt), scale)
         worst = max(worst, np.max(np.abs(got[idx] - want)))
     assert worst <= 2e-3, worst
+
+
+@pytest.mark.parametrize("part", [0, 64, 2048])
+def test_very_long_contexts(part):
+    """Maximum-size work: 64k-token contexts next to a one-token one, at the smallest,
+    default and largest partition sizes (up to 1,094 partitions of one sequence)."""
+    announce(f"long contexts 65536 / 70001 / 1, 64/8 heads bf16, partition {part}")
+    w = wl.custom_decode(77, wl.BF16, [65536, 70001, 1], 64, 8, block_size=16)
+    sess = DecodeSession(w, partition_tokens=part)
+    sess.step()
+    torch.cuda.synchronize()
+    assert torch.isfinite(sess.out).all()
+    check_against_oracle(sess, [0, 1, 2])

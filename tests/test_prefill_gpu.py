@@ -171,3 +171,13 @@ def test_block_size_that_is_not_a_power_of_two_is_rejected():
                               1 / math.sqrt(128), torch.zeros(1, 2, 128, dtype=torch.float32,
                                                               device="cuda"))
     assert e.value.code == pa.PA_E_UNSUPPORTED
+
+
+def test_prefill_over_a_long_prefix_merges_many_parts():
+    """A 16k-token prefix: each row's keys span 9 parts of 2048 (sampled rows)."""
+    announce("prefill over a 16384-token prefix (9 parts), bf16 32/8")
+    w = wl.custom_chunked(411, wl.BF16, [16384, 3], [256, 20], [], 32, 8, block_size=32)
+    sess = PrefillSession(w)
+    sess.step()
+    torch.cuda.synchronize()
+    check_chunks(sess, lambda i: [0, 1, 100, int(w.chunk_lens[i]) - 1] if i == 0 else range(int(w.chunk_lens[i])))
