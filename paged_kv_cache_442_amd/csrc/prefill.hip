@@ -326,16 +326,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 }
 
 // Log-sum-exp merge of a row block's parts, for row blocks with more than one: the same
-// (row block, sequence, KV head) grid, one thread per (column, 4 dims) item in turn.
+// (row block, sequence, KV head) grid with each row block's kMergeSlices workgroups side by
+// side, one thread per (column, 4 dims) item, so every thread's loads are independent.
 //   M = max_p lse_p,  w_p = 2^(lse_p - M),  out = sum_p w_p o_p / sum_p w_p
 // (the identity of the softmax over a union of key sets; o_p is part p's normalized
 // output, lse_p its base-2 log-sum-exp).  A NaN in any part makes the output NaN.
+constexpr int kMergeSlices = kCols * (kHead / 4) / 256;
+
 template <int G>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a) {
   constexpr int TR = kCols / G;
   const int seq = blockIdx.y;
   const int kvh = blockIdx.z;
-  const int r0 = blockIdx.x * TR;
+  const int r0 = (blockIdx.x / kMergeSlices) * TR;
   const int qs = a.query_start[seq];
   const int n_rows = a.query_start[seq + 1] - qs;
   if (r0 >= n_rows) return;
@@ -347,11 +350,12 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
   const int kmax = L - n_rows + min(r0 + TR, n_rows) - 1;
   const int n_parts = kmax / a.part_keys + 1;
   if (n_parts == 1) return;
-  for (int item = threadIdx.x; item < kCols * (kHead / 4); item += blockDim.x) {
+  {
+    const int item = (blockIdx.x % kMergeSlices) * 256 + threadIdx.x;
     const int col = item / (kHead / 4);
     const int d4 = (item % (kHead / 4)) * 4;
     const int row = r0 + col % TR;
-    if (row >= n_rows) continue;
+    if (row >= n_rows) return;
     const int64_t out_row = (static_cast<int64_t>(qs) + row) * a.num_q_heads + kvh * G + col / TR;
     const float* lse = a.part_lse + out_row * a.pmax;
     float M = -INFINITY;
@@ -405,7 +409,7 @@ hipError_t launch_prefill_merge(const PrefillArgs& a, int group, int max_query_l
   (void)hipGetLastError();
   if (a.pmax <= 1) return hipSuccess;
   const int tr = kCols / group;
-  const dim3 grid(static_cast<unsigned>((max_query_len + tr - 1) / tr),
+  const dim3 grid(static_cast<unsigned>((max_query_len + tr - 1) / tr * kMergeSlices),
                   static_cast<unsigned>(a.num_seqs), static_cast<unsigned>(a.num_kv_heads));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   switch (group) {
