@@ -303,7 +303,7 @@ def main():
             "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "num_blocks": w.num_blocks,
             "total_context_tokens": int(lens.sum()), "max_context": int(lens.max()),
-            "partition_tokens": args.partition or (1024 if w.num_q_heads // w.num_kv_heads >= 4 else 512),
+            "partition_tokens": args.partition or min(2048, 256 * (w.num_q_heads // w.num_kv_heads)),
             "block_placement": "contiguous" if args.contiguous_blocks else "seeded permutation",
             "kv_cache": "fp8-e4m3" if args.kv_fp8 else "same as q",
             "algorithmic_bytes_per_step": B,
@@ -382,7 +382,7 @@ def bench_window(args, torch, pa, sess, w, B, stream):
         "data": "synthetic (seeded N(0,1) K/V/Q, seeded block permutation)",
         "config": {"workload": args.workload + "_window", "window": args.window,
                    "algorithmic_bytes_per_step": B,
-                   "partition_tokens": args.partition or (1024 if w.num_q_heads // w.num_kv_heads >= 4 else 512)},
+                   "partition_tokens": args.partition or min(2048, 256 * (w.num_q_heads // w.num_kv_heads))},
         "tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
         "kernel_ms": {"decode_window (plan + partitions + merge)": round(dec_ms, 5)},
         "roofline": {"bound": "hbm", "kernel": "pa_decode_window", "achieved": round(achieved, 2),

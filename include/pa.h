@@ -293,7 +293,7 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
  *   "vLLM explained", two implementation layers: same result as ordinary attention).
  *
  * The work is split over partitions of `partition_tokens` consecutive tokens (0 =
- * default: 1024 for groups of 4 or 8 query heads per KV head, 512 otherwise; else a
+ * default: 256 tokens per query head of a KV head's group, at most 2048; else a
  * positive multiple of 64, at most 2048), run as three kernels
  * on `stream`:
  *   pa_decode_plan        lists the (sequence, partition) work items in the workspace

@@ -788,40 +788,62 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* s_tmp, int* tota
 }
 
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeArgs a) {
+  // Partial items are listed largest first (bucketed by their number of tiles), so that
+  // the smallest units are the last ones claimed and the persistent workgroups finish
+  // together.  The order of items within a bucket is whatever the LDS counters give:
+  // a unit's result does not depend on which workgroup runs it or when.
+  constexpr int kBuckets = kMaxPartition / kTileTokens + 1;  // 0: empty or invalid
   __shared__ int s_tmp[kPlanThreads / 64];
+  __shared__ int s_count[kBuckets];
+  __shared__ int s_next[kBuckets];
   const int P = a.partition_tokens;
-  auto classify = [&](int s, int* full, int* partial) {
+  auto classify = [&](int s, int* full, int* bucket) {
     const int L = a.ctx[s];
     const bool bad = L < 0 || L > a.max_context ||
                      static_cast<int64_t>(L) > static_cast<int64_t>(a.max_blocks) * a.block_size;
     if (bad || L == 0) {
       *full = 0;
-      *partial = 1;
+      *bucket = 0;
     } else {
       const int span = L - window_base(L, a.window);  // tokens from the first partition on
+      const int rem = span % P;
       *full = span / P;
-      *partial = (span % P) != 0;
+      *bucket = rem == 0 ? -1 : (rem + kTileTokens - 1) / kTileTokens;  // -1: no partial item
     }
   };
-  // Pass 1: the number of full items (the partial items are listed after them).
+  for (int b = threadIdx.x; b < kBuckets; b += blockDim.x) s_count[b] = 0;
+  __syncthreads();
+  // Pass 1: the number of full items, and the partial items per bucket.
   int full_total = 0;
   for (int s0 = 0; s0 < a.num_seqs; s0 += blockDim.x) {
     const int s = s0 + threadIdx.x;
-    int f = 0, pp = 0;
-    if (s < a.num_seqs) classify(s, &f, &pp);
+    int f = 0, b = -1;
+    if (s < a.num_seqs) classify(s, &f, &b);
+    if (b >= 0) atomicAdd(&s_count[b], 1);
     int t;
     block_exclusive_scan(f, s_tmp, &t);
     full_total += t;
   }
-  // Pass 2: positions, then the items themselves.
-  int full_base = 0, part_base = full_total;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int at = full_total;
+    for (int b = kBuckets - 1; b >= 0; --b) {
+      s_next[b] = at;
+      at += s_count[b];
+    }
+    s_tmp[0] = at;  // total items
+  }
+  __syncthreads();
+  const int n_items = s_tmp[0];
+  __syncthreads();
+  // Pass 2: the items themselves.
+  int full_base = 0;
   for (int s0 = 0; s0 < a.num_seqs; s0 += blockDim.x) {
     const int s = s0 + threadIdx.x;
-    int f = 0, pp = 0;
-    if (s < a.num_seqs) classify(s, &f, &pp);
-    int tf, tp;
+    int f = 0, b = -1;
+    if (s < a.num_seqs) classify(s, &f, &b);
+    int tf;
     const int fo = block_exclusive_scan(f, s_tmp, &tf) + full_base;
-    const int po = block_exclusive_scan(pp, s_tmp, &tp) + part_base;
     const int L = s < a.num_seqs ? a.ctx[s] : 0;
     for (int k = 0; k < f; ++k) {
       int32_t* d = a.work_items + 4 * (fo + k);
@@ -830,19 +852,18 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeA
       d[2] = L;
       d[3] = 0;
     }
-    if (pp) {
-      int32_t* d = a.work_items + 4 * po;
+    if (b >= 0) {
+      int32_t* d = a.work_items + 4 * atomicAdd(&s_next[b], 1);
       d[0] = s;
       d[1] = f;
       d[2] = L;
       d[3] = 0;
     }
     full_base += tf;
-    part_base += tp;
   }
   if (threadIdx.x == 0) {
     a.work_header[0] = 0;
-    a.work_header[1] = part_base * a.num_kv_heads;
+    a.work_header[1] = n_items * a.num_kv_heads;
   }
 }
 

@@ -12,14 +12,16 @@ namespace pa {
 constexpr int kHeadDim = 128;        // head_dim the attention kernels are built for
 constexpr int kTileTokens = 16;      // tokens per K/V tile streamed by the decode kernel
 constexpr int kDecodeWaves = 4;      // waves per decode workgroup
-// Default partition: groups of 4 or 8 query heads run the MFMA score path, whose units
-// carry a fixed end-of-unit merge that longer partitions amortize (measured 1024 best
-// for them); smaller groups balance better with 512.
-constexpr int default_partition(int group) { return group >= 4 ? 1024 : 512; }
 constexpr int kPlanThreads = 1024;
 // A wave's tiles of one unit must fit one wave of lanes; a workgroup has at least two
 // tile streams (four waves, at most two head halves).
 constexpr int kMaxPartition = 2 * 64 * kTileTokens;
+// Default partition: 256 tokens per query head of the group (a unit's time grows with
+// both), at most kMaxPartition.  Measured best on the Llama-shaped layers: 2048 for
+// groups of 8, 1024 for groups of 4, 256 for single heads.
+constexpr int default_partition(int group) {
+  return 256 * group < kMaxPartition ? 256 * group : kMaxPartition;
+}
 
 struct DecodeArgs {
   const void* q;            // [S][Hq][128]
