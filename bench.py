@@ -244,6 +244,7 @@ def main():
 
     part_avg_s = float(part_ms.mean()) * 1e-3
     achieved = B / part_avg_s / 1e9
+    part_tokens = args.partition or pa.pa_decode_default_partition(sess.pool, w.num_q_heads)
     value = B / (ms_step * 1e-3) / 1e9
 
     # sampled parity against the oracle on the timed output
@@ -303,7 +304,7 @@ def main():
             "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "num_blocks": w.num_blocks,
             "total_context_tokens": int(lens.sum()), "max_context": int(lens.max()),
-            "partition_tokens": args.partition or min(2048, 256 * (w.num_q_heads // w.num_kv_heads)),
+            "partition_tokens": part_tokens,
             "block_placement": "contiguous" if args.contiguous_blocks else "seeded permutation",
             "kv_cache": "fp8-e4m3" if args.kv_fp8 else "same as q",
             "algorithmic_bytes_per_step": B,
@@ -321,11 +322,11 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            # The committed counters belong to the default Llama-3-70B run only.
+            # The committed counters belong to the Llama-3-70B run at 2048-token partitions.
             "traffic": counter_traffic(os.path.dirname(os.path.abspath(__file__)))
             if (args.workload == "llama3_70b" and not args.kv_fp8 and not args.num_q_heads
                 and not args.fixed_len and not args.contiguous_blocks
-                and args.partition in (0, 1024)) else None,
+                and part_tokens == 2048) else None,
         },
         "copy_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
         "read_ceiling_GBps": None if rceiling is None else round(rceiling, 1),
@@ -382,7 +383,7 @@ def bench_window(args, torch, pa, sess, w, B, stream):
         "data": "synthetic (seeded N(0,1) K/V/Q, seeded block permutation)",
         "config": {"workload": args.workload + "_window", "window": args.window,
                    "algorithmic_bytes_per_step": B,
-                   "partition_tokens": args.partition or min(2048, 256 * (w.num_q_heads // w.num_kv_heads))},
+                   "partition_tokens": args.partition or pa.pa_decode_default_partition(sess.pool, w.num_q_heads)},
         "tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
         "kernel_ms": {"decode_window (plan + partitions + merge)": round(dec_ms, 5)},
         "roofline": {"bound": "hbm", "kernel": "pa_decode_window", "achieved": round(achieved, 2),

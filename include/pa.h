@@ -293,8 +293,8 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
  *   "vLLM explained", two implementation layers: same result as ordinary attention).
  *
  * The work is split over partitions of `partition_tokens` consecutive tokens (0 =
- * default: 256 tokens per query head of a KV head's group, at most 2048; else a
- * positive multiple of 64, at most 2048), run as three kernels
+ * default: pa_decode_default_partition; else a positive multiple of 64, at most 2048),
+ * run as three kernels
  * on `stream`:
  *   pa_decode_plan        lists the (sequence, partition) work items in the workspace
  *                         and zeroes its work counter;
@@ -326,6 +326,12 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
  * any block_size that is a multiple of 16; all dtypes (fp32 accumulation). */
 int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context, int32_t partition_tokens);
+/* The partition size a decode call with partition_tokens = 0 uses for this pool and
+ * num_q_heads (host only, no GPU call): for fp32/fp16/bf16 caches 256 tokens per query
+ * head of a KV head's group, at most 2048; for an e4m3 cache 512 tokens for groups of 1
+ * and 2 and 1024 for groups of 4 and 8.  Returns PA_E_INVAL (negative) for a NULL pool or
+ * num_q_heads that is not a positive multiple of num_kv_heads. */
+int32_t pa_decode_default_partition(const pa_pool* pool, int32_t num_q_heads);
 int pa_decode_plan(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
                    int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
                    const int32_t* context_lens, int32_t max_context, float scale,

@@ -62,6 +62,7 @@ _SIGNATURES = {
     "pa_reshape_and_cache": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, _I32, _P]),
     "pa_decode_workspace_bytes": (_I64, [_P, _I32, _I32, _I32, _I32]),
+    "pa_decode_default_partition": (_I32, [_P, _I32]),
     "pa_decode": (ctypes.c_int, _DECODE_ARGS),
     "pa_decode_plan": (ctypes.c_int, _DECODE_ARGS),
     "pa_decode_partitions": (ctypes.c_int, _DECODE_ARGS),
@@ -433,6 +434,10 @@ def pa_copy_blocks(pool, pairs, stream=None):
     n = pairs.shape[0] if pairs.numel() else 0
     _check(lib().pa_copy_blocks(pool.handle, _dev(pairs, torch.int32, "pairs") if n else None, n,
                                 _stream(stream)))
+
+
+def pa_decode_default_partition(pool, num_q_heads):
+    return _check(lib().pa_decode_default_partition(pool.handle, num_q_heads))
 
 
 def pa_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_context, partition_tokens=0):

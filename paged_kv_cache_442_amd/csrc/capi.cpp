@@ -98,6 +98,17 @@ int check_device_pool(const pa_pool* p, int32_t layer) {
 // Workspace: [work header | work items | partition outputs | partition log-sum-exps].
 constexpr int64_t kWorkHeaderBytes = 256;
 
+// Default partition, measured best on the Llama-shaped layers.  A unit's fixed cost
+// (descriptor, query rows, the merge of its waves, the partial's write) grows with the
+// group, so 16- and 32-bit caches take 256 tokens per query head of the group, at most
+// pa::kMaxPartition (2048 for groups of 8, 256 for single heads).  An e4m3 tile is half the
+// bytes, so groups of 1 and 2 take 512 tokens; groups of 4 and 8 convert every element
+// and are compute-heavy, and 1024 tokens balance the persistent grid better there.
+int default_partition(int group, int elem_bytes) {
+  if (elem_bytes == 1) return group <= 2 ? 512 : 1024;
+  return 256 * group < pa::kMaxPartition ? 256 * group : pa::kMaxPartition;
+}
+
 int64_t items_bytes(int64_t num_seqs, int64_t pmax) {
   return (num_seqs * pmax * 16 + 255) / 256 * 256;
 }
@@ -131,7 +142,7 @@ int prepare_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs
   if (d.block_size % pa::kTileTokens != 0)
     return fail(PA_E_UNSUPPORTED, "block_size %d (must be a multiple of %d)", d.block_size,
                 pa::kTileTokens);
-  if (partition_tokens == 0) partition_tokens = pa::default_partition(group);
+  if (partition_tokens == 0) partition_tokens = default_partition(group, static_cast<int>(pool->elem_bytes));
   if (partition_tokens < 0 || partition_tokens % (pa::kTileTokens * pa::kDecodeWaves) != 0 ||
       partition_tokens > pa::kMaxPartition)
     return fail(PA_E_INVAL, "partition_tokens %d must be a positive multiple of %d, at most %d",
@@ -482,6 +493,15 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
                     "pa_copy_blocks");
 }
 
+int32_t pa_decode_default_partition(const pa_pool* pool, int32_t num_q_heads) {
+  if (!pool) return fail(PA_E_INVAL, "pool is NULL");
+  const int32_t hkv = pool->desc.num_kv_heads;
+  if (num_q_heads < 1 || num_q_heads % hkv != 0)
+    return fail(PA_E_INVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, hkv);
+  return default_partition(num_q_heads / hkv, static_cast<int>(pool->elem_bytes));
+}
+
 int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context, int32_t partition_tokens) {
   if (!pool) return fail(PA_E_INVAL, "pool is NULL");
@@ -489,7 +509,8 @@ int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t
     return fail(PA_E_INVAL, "negative size");
   if (partition_tokens == 0) {
     const int32_t hkv = pool->desc.num_kv_heads;
-    partition_tokens = pa::default_partition(hkv > 0 ? num_q_heads / hkv : 1);
+    partition_tokens = default_partition(hkv > 0 ? num_q_heads / hkv : 1,
+                                             static_cast<int>(pool->elem_bytes));
   }
   const int64_t pmax =
       std::max<int64_t>(1, (static_cast<int64_t>(max_context) + partition_tokens - 1) / partition_tokens);

@@ -16,12 +16,6 @@ constexpr int kPlanThreads = 1024;
 // A wave's tiles of one unit must fit one wave of lanes; a workgroup has at least two
 // tile streams (four waves, at most two head halves).
 constexpr int kMaxPartition = 2 * 64 * kTileTokens;
-// Default partition: 256 tokens per query head of the group (a unit's time grows with
-// both), at most kMaxPartition.  Measured best on the Llama-shaped layers: 2048 for
-// groups of 8, 1024 for groups of 4, 256 for single heads.
-constexpr int default_partition(int group) {
-  return 256 * group < kMaxPartition ? 256 * group : kMaxPartition;
-}
 
 struct DecodeArgs {
   const void* q;            // [S][Hq][128]

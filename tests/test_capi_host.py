@@ -248,3 +248,25 @@ def test_prefill_workspace_is_needed_only_past_one_part():
     items = rows * heads * pmax
     lse = -(-items * 4 // 256) * 256
     assert pa.pa_prefill_workspace_bytes(pool, rows, heads, 4097) == lse + items * 128 * 4
+
+
+def test_decode_default_partition():
+    # 16- and 32-bit caches: 256 tokens per query head of the group, at most 2048; e4m3:
+    # 512 for groups of 1 and 2, 1024 for groups of 4 and 8.
+    want = {pa.F32: [256, 512, 1024, 2048], pa.F16: [256, 512, 1024, 2048],
+            pa.BF16: [256, 512, 1024, 2048], pa.FP8_E4M3: [512, 512, 1024, 1024]}
+    for dt, parts in want.items():
+        pool = pa.pa_alloc_pool(pa.make_desc(1, 4, 16, 8, 128, dt), None, None)
+        try:
+            got = [pa.pa_decode_default_partition(pool, 8 * g) for g in (1, 2, 4, 8)]
+            assert got == parts, (dt, got)
+            # a workspace sized for partition 0 is the one sized for the default
+            S, ctx = 3, 5000
+            for g, part in zip((1, 2, 4, 8), parts):
+                assert (pa.pa_decode_workspace_bytes(pool, S, 8 * g, ctx)
+                        == pa.pa_decode_workspace_bytes(pool, S, 8 * g, ctx, part))
+            for bad in (0, -8, 12):
+                with pytest.raises(pa.PAError):
+                    pa.pa_decode_default_partition(pool, bad)
+        finally:
+            pa.pa_free_pool(pool)
