@@ -329,11 +329,14 @@ struct Unit {
 };
 
 // Persistent decode workgroups.  Each claims work numbers (item, KV head) from the
-// counter the plan kernel zeroed, one ahead of the one it runs, until they run out.
-// While a unit runs, the next one is made ready: its descriptor (scalar loads), the
-// row offsets of its tiles, its query rows (staged through LDS) and its first two K/V
-// tiles (issued by the last iterations of the current tile loop), so consecutive units
-// run back to back.
+// counter the plan kernel zeroed until they run out.  The next unit is claimed late in
+// the current one, a few steps before its end (wave 0 takes the number and hands it to
+// the other waves through LDS), so that no workgroup holds work that an idle one could
+// run: the list ends on its smallest items, and those go to whichever workgroups free
+// up first.  The claim still comes early enough for the next unit to be made ready
+// while the current one runs: its descriptor (scalar loads), the row offsets of its
+// tiles, its query rows (staged through LDS) and its first K/V step (issued by the
+// last step of the current tile loop), so consecutive units run back to back.
 // Workgroups per CU the register budget is sized for: the more query heads a wave
 // carries (query and output registers), the fewer workgroups fit.
 template <class E, int GW>
@@ -371,7 +374,9 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
 
   __shared__ Lds lds;
   __shared__ u32x4 s_q[G * NCH];  // query rows of the next unit
-  __shared__ int s_claim[2];
+  __shared__ int s_claim;       // the first unit's work number
+  __shared__ int s_next_work;   // the next unit's work number, published by wave 0 ...
+  __shared__ int s_next_epoch;  // ... for the unit with this count (units started so far)
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -404,10 +409,11 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     return (is_bad(u) || u.L == 0) ? t_begin_of(u) : min(u.L, t_begin_of(u) + P);
   };
   // Number of tiles this wave takes in a unit (tiles stream, stream + NS, ...).
-  auto wave_tiles = [&](const Unit& u) {
+  auto wave_tiles_of_stream = [&](const Unit& u, int st) {
     const int n_tiles = (t_end_of(u) - t_begin_of(u) + kTileTokens - 1) / kTileTokens;
-    return stream < n_tiles ? (n_tiles - stream + NS - 1) / NS : 0;
+    return st < n_tiles ? (n_tiles - st + NS - 1) / NS : 0;
   };
+  auto wave_tiles = [&](const Unit& u) { return wave_tiles_of_stream(u, stream); };
   // Row offset (rows of head_dim elements from the layer's K base) of the wave's tile
   // `lane`, or -1 if its block id lies outside the pool; 0 for lanes past the wave's
   // tiles.  partition_tokens <= kMaxPartition keeps a wave's tiles within 64 lanes.
@@ -437,16 +443,16 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
   };
 
   if (tid == 0) {
-    s_claim[0] = atomicAdd(a.work_header, 1);
-    s_claim[1] = atomicAdd(a.work_header, 1);
+    s_claim = atomicAdd(a.work_header, 1);
+    s_next_epoch = 0;
   }
   __syncthreads();
   const int n_work = ld_uniform(a.work_header, 1);
-  int cur = __builtin_amdgcn_readfirstlane(s_claim[0]);
-  int nxt = __builtin_amdgcn_readfirstlane(s_claim[1]);
-  if (cur >= n_work) return;
+  const int first = __builtin_amdgcn_readfirstlane(s_claim);
+  if (first >= n_work) return;
+  int epoch = 0;  // units started so far
 
-  Unit it = unit_of(cur);
+  Unit it = unit_of(first);
   int nt = wave_tiles(it);
   int rows_cur = tile_rows(it, nt);
   {
@@ -460,14 +466,8 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
   const char* vbase = static_cast<const char*>(a.v_cache);
 
   while (true) {
-    __syncthreads();  // s_q is staged; s_claim and the previous unit's LDS are free
-    // The claim's result is needed only at the end of the unit: it stays in a register
-    // until then, so that nothing waits for the atomic here.
-    int claimed = 0;
-    if (tid == 0) claimed = atomicAdd(a.work_header, 1);
-    const bool has_next = nxt < n_work;
-    const Unit nx = unit_of(has_next ? nxt : cur);
-    const int nt_nx = has_next ? wave_tiles(nx) : 0;
+    __syncthreads();  // s_q is staged; every wave has read s_next_*; the LDS is free
+    ++epoch;
     const int t_begin = t_begin_of(it);
     const int t_end = t_end_of(it);
     const int t_lo = window_start(it.L, a.window);  // tokens before it are outside the window
@@ -489,10 +489,11 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
       }
     }
 
-    // Tile n of the wave's stream: this unit's tiles, then (when the next unit has
-    // tiles on this wave) the next unit's first one; else this unit's last tile again
-    // (a cache hit), so every pass has the same loads in flight and the same waits.
-    const bool cross = nt_nx > 0;
+    // The next unit, known from the step at which this wave loads it (load_next).
+    bool has_next = false;
+    Unit nx = it;
+    int nt_nx = 0;
+    bool cross = false;  // the next unit has tiles on this wave: its first step is prefetched
     int rows_next = 0;
     // A block id outside the pool (row offset -1) makes the unit's result NaN; such
     // tiles are read from block 0 instead, so nothing outside the pool is touched.
@@ -530,12 +531,42 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
       }
     };
 
-    // The next unit's row offsets and query rows, loaded once this unit is under way.
+    // Wave 0 claims the next unit at step claim_step of its stream and publishes the
+    // number at its load step; every wave loads the next unit (descriptor, row offsets,
+    // query rows) at its own load step, waiting for the publication if it gets there
+    // first.  Both steps sit a few steps before the end, so that the next unit's first
+    // step can be issued by this unit's last one; short units do both at step 0.
+    constexpr int kClaimLead = 6 / TS, kLoadLead = 4 / TS;
+    const int ns0 = (wave_tiles_of_stream(it, 0) + TS - 1) / TS;  // wave 0's steps
+    const int claim_step = max(0, ns0 - kClaimLead);
+    const int load_step = max(0, ns - kLoadLead);
+    int claimed = 0;
+    bool claim_done = false;
+    auto claim = [&]() {
+      if (tid == 0) claimed = atomicAdd(a.work_header, 1);
+      claim_done = true;
+    };
     uint32_t qn[QPT];
     bool next_loaded = false;
     auto load_next = [&]() {
-      rows_next = has_next ? tile_rows(nx, nt_nx) : 0;
-      if (has_next) load_q(nx, qn);
+      if (wave == 0) {
+        if (!claim_done) claim();
+        if (tid == 0) {
+          s_next_work = claimed;
+          __hip_atomic_store(&s_next_epoch, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+      while (__hip_atomic_load(&s_next_epoch, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != epoch)
+        __builtin_amdgcn_s_sleep(1);
+      const int nxt = __builtin_amdgcn_readfirstlane(s_next_work);
+      has_next = nxt < n_work;
+      if (has_next) {
+        nx = unit_of(nxt);
+        nt_nx = wave_tiles(nx);
+        cross = nt_nx > 0;
+        rows_next = tile_rows(nx, nt_nx);
+        load_q(nx, qn);
+      }
       next_loaded = true;
     };
 
@@ -557,6 +588,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     auto process = [&](int n) {
       // First token of tile u of this step, and the token of a lane's value i in it
       // (score i, and V load i's row).
+      if (wave == 0 && n == claim_step) claim();
       auto tile_t0 = [&](int u) { return t_begin + (stream + NS * (TS * n + u)) * kTileTokens; };
       auto token = [&](int u, int i) {
         return MF ? tile_t0(u) + 4 * rr + i : tile_t0(u) + i * TG + rr;
@@ -570,7 +602,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
 #pragma unroll
           for (int k = 0; k < 4; ++k) acc[u] = E::mma16(E::k_operand(kr[u * LOADS + k]), qv[k], acc[u]);
         }
-        if (n == 0) load_next();
+        if (n == load_step) load_next();
         issue(n + 1, kbase, kr, k_off, k_step);
 #pragma unroll
         for (int u = 0; u < TS; ++u)
@@ -594,7 +626,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
             s[i][p] = E::dot(qv[p].w, kk.w, acc);
           }
         }
-        if (n == 0) load_next();
+        if (n == load_step) load_next();
         issue(n + 1, kbase, kr, k_off, k_step);
         if constexpr (NCH == 32) {
           // A row spans two DPP rows: add the other half of the row first.
@@ -750,10 +782,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     }
     if (!has_next) break;
     stage_q(qn);  // s_q was last read at this unit's start, before a barrier
-    if (tid == 0) s_claim[0] = claimed;
-    __syncthreads();  // s_claim[0] is visible; the merge is done with lds
-    cur = nxt;
-    nxt = __builtin_amdgcn_readfirstlane(s_claim[0]);
+    __syncthreads();  // the merge is done with lds
     it = nx;
     nt = nt_nx;
     rows_cur = rows_next;
