@@ -327,10 +327,10 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
 int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context, int32_t partition_tokens);
 /* The partition size a decode call with partition_tokens = 0 uses for this pool and
- * num_q_heads (host only, no GPU call): for fp32/fp16/bf16 caches 256 tokens per query
- * head of a KV head's group, at most 2048; for an e4m3 cache 512 tokens for groups of 1
- * and 2 and 1024 for groups of 4 and 8.  Returns PA_E_INVAL (negative) for a NULL pool or
- * num_q_heads that is not a positive multiple of num_kv_heads. */
+ * num_q_heads (host only, no GPU call): 2048 tokens for fp16, bf16 and e4m3 caches at
+ * groups (num_q_heads / num_kv_heads) of 4 or 8; otherwise 1024 / element bytes tokens
+ * (512 for fp16/bf16, 1024 for e4m3, 256 for fp32).  Returns PA_E_INVAL (negative) for a
+ * NULL pool or num_q_heads that is not a positive multiple of num_kv_heads. */
 int32_t pa_decode_default_partition(const pa_pool* pool, int32_t num_q_heads);
 int pa_decode_plan(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
                    int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,

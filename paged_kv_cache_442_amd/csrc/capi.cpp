@@ -98,15 +98,15 @@ int check_device_pool(const pa_pool* p, int32_t layer) {
 // Workspace: [work header | work items | partition outputs | partition log-sum-exps].
 constexpr int64_t kWorkHeaderBytes = 256;
 
-// Default partition, measured best on the Llama-shaped layers.  A unit's fixed cost
-// (descriptor, query rows, the merge of its waves, the partial's write) grows with the
-// group, so 16- and 32-bit caches take 256 tokens per query head of the group, at most
-// pa::kMaxPartition (2048 for groups of 8, 256 for single heads).  An e4m3 tile is half the
-// bytes, so groups of 1 and 2 take 512 tokens; groups of 4 and 8 convert every element
-// and are compute-heavy, and 1024 tokens balance the persistent grid better there.
+// Default partition, measured best on the Llama-shaped layers.  Workgroups claim their
+// next unit only near the end of the current one, so long units cost little at the end
+// of the grid and the fixed cost of a unit (descriptor, query rows, the merge of its
+// waves, the partial's write) decides.  The MFMA path (16-bit queries, groups of 4 or 8)
+// has the larger fixed cost and takes the largest partition; the vector path takes
+// 256 KiB of K and V per KV head (512 tokens of fp16/bf16, 1024 of e4m3, 256 of fp32).
 int default_partition(int group, int elem_bytes) {
-  if (elem_bytes == 1) return group <= 2 ? 512 : 1024;
-  return 256 * group < pa::kMaxPartition ? 256 * group : pa::kMaxPartition;
+  if (elem_bytes <= 2 && group >= 4) return pa::kMaxPartition;
+  return 1024 / elem_bytes;
 }
 
 int64_t items_bytes(int64_t num_seqs, int64_t pmax) {

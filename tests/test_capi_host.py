@@ -251,10 +251,9 @@ def test_prefill_workspace_is_needed_only_past_one_part():
 
 
 def test_decode_default_partition():
-    # 16- and 32-bit caches: 256 tokens per query head of the group, at most 2048; e4m3:
-    # 512 for groups of 1 and 2, 1024 for groups of 4 and 8.
-    want = {pa.F32: [256, 512, 1024, 2048], pa.F16: [256, 512, 1024, 2048],
-            pa.BF16: [256, 512, 1024, 2048], pa.FP8_E4M3: [512, 512, 1024, 1024]}
+    # 2048 tokens for 16-bit and e4m3 caches at groups of 4 and 8, else 1024 / element bytes.
+    want = {pa.F32: [256, 256, 256, 256], pa.F16: [512, 512, 2048, 2048],
+            pa.BF16: [512, 512, 2048, 2048], pa.FP8_E4M3: [1024, 1024, 2048, 2048]}
     for dt, parts in want.items():
         pool = pa.pa_alloc_pool(pa.make_desc(1, 4, 16, 8, 128, dt), None, None)
         try:
