@@ -83,6 +83,15 @@ def counter_traffic(root):
                      rec["write_kib_per_launch"] * 1024 * rec["write_scale"]))
 
 
+def worse_err(worst, got, want):
+    """The larger of ``worst`` and the largest |got - want|; NaN anywhere counts as inf
+    (``max`` would drop it)."""
+    d = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(want, dtype=np.float64))
+    if not np.all(np.isfinite(d)):
+        return float("inf")
+    return max(worst, float(d.max()))
+
+
 def make_workload(name, num_q_heads=None, fixed_len=0):
     from paged_kv_cache_442_amd import workloads as wl
     if name == "llama3_70b" and (num_q_heads or fixed_len):
@@ -287,7 +296,7 @@ def main():
         want = attention.contiguous_decode(w.dtype, w.q[s], cache_values(kt, sess.k_scale),
                                            cache_values(vt, sess.v_scale),
                                            attention.default_scale(w.head_dim))
-        worst = max(worst, float(np.max(np.abs(got[s] - want))))
+        worst = worse_err(worst, got[s], want)
 
     # host block manager: one appended token per sequence (A1), on a host-only pool
     hp = pa.pa_alloc_pool(pa.make_desc(1, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
@@ -395,7 +404,7 @@ def bench_window(args, torch, pa, sess, w, B, stream):
         want = attention.window_decode(w.dtype, w.q[s_], fpbits.decode(w.dtype, kt),
                                        fpbits.decode(w.dtype, vt), attention.default_scale(w.head_dim),
                                        args.window)
-        worst = max(worst, float(np.max(np.abs(got[s_] - want))))
+        worst = worse_err(worst, got[s_], want)
     achieved = B / (dec_ms * 1e-3) / 1e9
     line = {
         "metric": "paged-decode KV GB/s and % of HBM peak at 1 MI355X; tokens/sec per layer",
@@ -491,11 +500,11 @@ def bench_mixed(args, torch):
             pos = int(w.prefix_lens[i]) + r
             want = attention.contiguous_decode(w.dtype, w.q_chunks[int(w.chunk_offsets[i]) + r],
                                                kc[:pos + 1], vc[:pos + 1], scale)
-            worst = max(worst, float(np.max(np.abs(got_c[int(w.chunk_offsets[i]) + r] - want))))
+            worst = worse_err(worst, got_c[int(w.chunk_offsets[i]) + r], want)
     for j in sorted({0, sess.n_decode - 1}):
         kc, vc = seq_kv(sess.n_chunks + j)
         want = attention.contiguous_decode(w.dtype, w.q_decode[j], kc, vc, scale)
-        worst = max(worst, float(np.max(np.abs(got_d[j] - want))))
+        worst = worse_err(worst, got_d[j], want)
     rows = int(np.sum(w.chunk_lens)) + sess.n_decode
     line = {
         "metric": "paged-decode KV GB/s and % of HBM peak at 1 MI355X; tokens/sec per layer",
@@ -588,7 +597,7 @@ def bench_shared_prefix(args, torch):
         kt, vt = sess.branch_tokens(s_)
         want = attention.contiguous_decode(w.dtype, w.q[sess.branch_of[s_]], fpbits.decode(w.dtype, kt),
                                            fpbits.decode(w.dtype, vt), attention.default_scale(d))
-        worst = max(worst, float(np.max(np.abs(got[idx] - want))))
+        worst = worse_err(worst, got[idx], want)
     value = B / (dec_ms * 1e-3) / 1e9
     line = {
         "metric": "paged-decode KV GB/s and % of HBM peak at 1 MI355X; tokens/sec per layer",
@@ -678,7 +687,7 @@ def bench_swap(args, torch):
         kt, vt = w.seq_tokens(s_)
         want = attention.contiguous_decode(w.dtype, w.q[s_], fpbits.decode(w.dtype, kt),
                                            fpbits.decode(w.dtype, vt), attention.default_scale(w.head_dim))
-        worst = max(worst, float(np.max(np.abs(got[s_] - want))))
+        worst = worse_err(worst, got[s_], want)
     # Ceiling: one contiguous DMA copy of the same size each way.
     dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     hview = host[:nbytes]
@@ -770,7 +779,7 @@ def bench_prefix_cache(args, torch):
         k, v = w.kv_rows(toks, np.arange(len(toks)))
         want = attention.contiguous_decode(w.dtype, w.q[live[j]], fpbits.decode(w.dtype, k),
                                            fpbits.decode(w.dtype, v), attention.default_scale(d))
-        worst = max(worst, float(np.max(np.abs(got[j] - want))))
+        worst = worse_err(worst, got[j], want)
 
     prompt_tokens = sum(len(w.prompt(i)) for i in range(w.num_requests))
     cached = int(sess.cached_tokens.sum())

@@ -341,8 +341,8 @@ struct Unit {
 // carries (query and output registers), the fewer workgroups fit.
 template <class E, int GW>
 constexpr int decode_blocks_per_cu() {
-  // GW >= 4 with 16-bit queries runs the MFMA path, which keeps two tiles of K and V in
-  // flight per wave: two workgroups fit.
+  // GW >= 4 with 16-bit queries runs the MFMA path; its LDS (g = 8) or, at g = 4, the
+  // memory system allows two workgroups (a third or fourth measured no faster or slower).
   return E::kBytes == 4 ? 2 : (GW >= 4 ? 2 : 4);
 }
 
@@ -367,8 +367,12 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
   // the row that holds the V values they weight, and PV is the same row-broadcast FMA.
   constexpr bool MF = E::kQBytes == 2 && GW >= 4 && HS == 1;
   static_assert(!MF || (NCH == 16 && LOADS == 4), "MFMA scores assume 16-lane rows, 4 loads");
-  // Tiles per step: the MFMA path has the registers to keep two tiles' K and V in flight.
-  constexpr int TS = MF ? 2 : 1;
+  // Tiles per step (each wave keeps one step's K and V in flight).  The MFMA path has the
+  // registers for two, but with 16-bit K/V the chip then has about 32 MiB of reads in
+  // flight, more than the memory system serves best: one tile per step measured 4% faster
+  // at g = 8.  An e4m3 tile is half the bytes; at g = 4 two of them per step measured 4%
+  // faster, while at g = 8 the conversions and FMAs bound the kernel and one is faster.
+  constexpr int TS = (MF && E::kBytes == 1 && GW == 4) ? 2 : 1;
   constexpr int NL = TS * LOADS;  // K (and V) loads per step
   constexpr int64_t kRowBytes = kHeadDim * E::kBytes;
 

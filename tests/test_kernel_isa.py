@@ -1,4 +1,4 @@
-"""The decode kernel's hand-placed DPP instructions, checked in its compiled gfx950 code.
+"""Properties of the kernels' compiled gfx950 code that the compiler does not guarantee.
 
 1. The PV step reads each probability through a DPP row broadcast inside an inline-asm
 FMA, which the compiler's hazard recognizer cannot see; the kernel therefore places
@@ -10,6 +10,11 @@ the FMA read a stale value.  Every DPP instruction is checked.
 own.  A bit cast of a vector element taken as an lvalue once made the compiler widen
 element 0 four times.  A 16-token tile is 4 wave-wide loads of 4 rows, so the fp16
 kernels must convert from 4 x 4 = 16 distinct registers (the faulty code used 4).
+
+3. No kernel keeps values in the accumulation registers (AGPRs).  The one build that did
+(the decode kernel for groups of 8 compiled for three workgroups per CU, which moved the
+MFMA accumulators there) gave wrong outputs at g = 8 on the GPU, and no cause was found
+in its code; the kernels stay in VGPRs.
 
 The kernels are compiled to assembly with the library's own flags; hipcc is needed,
 not a GPU.
@@ -34,11 +39,16 @@ def asm(tmp_path_factory):
     return compile_to_asm(tmp_path_factory.mktemp("isa"))
 
 
-def compile_to_asm(tmp_path):
-    out = tmp_path / "kernels.s"
+@pytest.fixture(scope="module")
+def prefill_asm(tmp_path_factory):
+    return compile_to_asm(tmp_path_factory.mktemp("isa_prefill"), "prefill.hip")
+
+
+def compile_to_asm(tmp_path, source="kernels.hip"):
+    out = tmp_path / (source + ".s")
     flags = [f for f in build.HIP_FLAGS if f not in ("-shared", "-fPIC")]
     cmd = [build.hipcc()] + flags + ["--cuda-device-only", "-S", "-I", build.INCLUDE, "-I", build.CSRC,
-                                     os.path.join(build.CSRC, "kernels.hip"), "-o", str(out)]
+                                     os.path.join(build.CSRC, source), "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     return out.read_text()
@@ -121,3 +131,22 @@ def test_the_widen_scan_catches_one_dword_widened_four_times():
     body = "\n".join(["v_cvt_f32_f16_sdwa v73, v30 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1",
                       "v_cvt_f32_f16_e32 v74, v30"] * 4)
     assert f16_widen_sources(body) == {"v30"}
+
+
+def agpr_use(asm):
+    """(largest .agpr_count in the kernel metadata, number of AGPR copy instructions)."""
+    counts = [int(c) for c in re.findall(r"\.agpr_count:\s+(\d+)", asm)]
+    copies = sum(1 for line in instructions(asm) if line.split()[0].startswith("v_accvgpr"))
+    return (max(counts) if counts else 0), copies, len(counts)
+
+
+def test_no_kernel_uses_agprs(asm, prefill_asm):
+    for text in (asm, prefill_asm):
+        most, copies, n = agpr_use(text)
+        assert n > 0
+        assert most == 0 and copies == 0, (most, copies)
+
+
+def test_the_agpr_scan_sees_an_accumulator_copy():
+    text = "\n".join(["  - .agpr_count:     4", "v_accvgpr_read_b32 v21, a3"])
+    assert agpr_use(text) == (4, 1, 1)
