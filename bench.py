@@ -83,6 +83,50 @@ def counter_traffic(root):
                      rec["write_kib_per_launch"] * 1024 * rec["write_scale"]))
 
 
+class FenceFreeEvents:
+    """HIP timing events recorded without the system-scope memory fence
+    (``hipEventDisableSystemFence``): a default event record writes back and invalidates
+    the caches, which costs the stream several microseconds and slows the kernel after
+    it.  These events only time the stream; the results are read after a device-wide
+    synchronize.  They come from the HIP runtime torch has loaded (one runtime per
+    process)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, count):
+        import ctypes
+        import torch
+        torch.cuda.init()
+        path = next(line.split()[-1] for line in open("/proc/self/maps")
+                    if "libamdhip64" in line and line.split()[-1].startswith("/"))
+        self.hip = ctypes.CDLL(path)
+        self.c = ctypes
+        self.ev = []
+        for _ in range(count):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+            self.ev.append(e)
+
+    def record(self, i, stream):
+        rc = self.hip.hipEventRecord(self.ev[i], self.c.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % rc)
+
+    def elapsed_ms(self, i, j):
+        ms = self.c.c_float()
+        rc = self.hip.hipEventElapsedTime(self.c.byref(ms), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
 def worse_err(worst, got, want):
     """The larger of ``worst`` and the largest |got - want|; NaN anywhere counts as inf
     (``max`` would drop it)."""
@@ -227,9 +271,9 @@ def main():
 
     n = args.steps
     # The timed region: K steps.  The only events inside it bracket the partition kernel,
-    # whose duration the roofline needs (an event record costs the stream a few
-    # microseconds, so the step time carries these two).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    # whose duration the roofline needs; they skip the system-scope fence (see
+    # FenceFreeEvents), and the step time carries what they still cost.
+    ev = FenceFreeEvents(2 * n)
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -237,15 +281,16 @@ def main():
     for i in range(n):
         sess.write_new_tokens()
         sess.decode_plan()
-        ev[i][0].record(stream)
+        ev.record(2 * i, stream)
         sess.decode_partitions()
-        ev[i][1].record(stream)
+        ev.record(2 * i + 1, stream)
         sess.decode_reduce()
     t_stop.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_stop)
     ms_step = total_ms / n
-    part_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    part_ms = np.array([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(n)])
+    ev.close()
 
     # Outside the timed region: the other kernels' times (events around every kernel) and
     # the step time with no events inside the loop at all.
@@ -383,18 +428,19 @@ def bench_window(args, torch, pa, sess, w, B, stream):
         decode()
     torch.cuda.synchronize()
     n = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    ev = FenceFreeEvents(2 * n)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(n):
         sess.write_new_tokens()
-        ev[i][0].record(stream)
+        ev.record(2 * i, stream)
         decode()
-        ev[i][1].record(stream)
+        ev.record(2 * i + 1, stream)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / n
-    dec_ms = float(np.mean([x[0].elapsed_time(x[1]) for x in ev]))
+    dec_ms = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(n)]))
+    ev.close()
     from oracle import attention, fpbits
     got = sess.out.cpu().numpy().astype(np.float64)
     lens = np.asarray(w.context_lens)
@@ -453,22 +499,23 @@ def bench_mixed(args, torch):
     torch.cuda.synchronize()
     n = args.steps
     # The timed region: events only around the prefill and decode calls.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    ev = FenceFreeEvents(3 * n)
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(n):
         sess.write_step_tokens()
-        ev[i][0].record(stream)
+        ev.record(3 * i, stream)
         sess.prefill()
-        ev[i][1].record(stream)
+        ev.record(3 * i + 1, stream)
         sess.decode()
-        ev[i][2].record(stream)
+        ev.record(3 * i + 2, stream)
     t_stop.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_stop) / n
-    prefill_ms = float(np.mean([x[0].elapsed_time(x[1]) for x in ev]))
-    decode_ms = float(np.mean([x[1].elapsed_time(x[2]) for x in ev]))
+    prefill_ms = float(np.mean([ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(n)]))
+    decode_ms = float(np.mean([ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(n)]))
+    ev.close()
     # outside it: the cache write's time
     wev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(min(n, 20))]
     for e in wev:
