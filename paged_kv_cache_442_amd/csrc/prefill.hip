@@ -39,10 +39,10 @@ constexpr int kCols = 128;    // (row, head) columns per workgroup
 constexpr int kKRow = kHead + 8;   // K tile row stride in LDS (elements), against bank conflicts
 constexpr int kVRow = kKeys + 8;   // transposed V tile row stride (elements)
 constexpr float kRescaleSlack = 8.0f;
-constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters left alone
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -73,6 +73,7 @@ __device__ __forceinline__ uint32_t pack2(T lo, T hi) {
 template <class M, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   using T = typename M::elem;
+  typedef T T2 __attribute__((ext_vector_type(2)));
   constexpr int TR = kCols / G;  // query rows per workgroup
   constexpr int kTileK = kKeys * kKRow;
   constexpr int kTileV = kHead * kVRow;
@@ -153,35 +154,45 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int bmask = a.block_size - 1;
   bool bad_blk = false;
   auto tile_block = [&](int t) -> int { return tbl[min(t * kKeys + sk, kmax) >> sh]; };
-  auto issue = [&](int t, int phys, u32x4 (&kr)[2], u32x4 (&vr)[2], int& valid) {
-    const int key = t * kKeys + sk;
-    valid = (key <= kmax ? 1 : 0) | (key + 1 <= kmax ? 2 : 0);
+  // Global address (elements) of this thread's two rows of tile t, given the tile's block.
+  auto tile_rows = [&](int t, int phys) -> int64_t {
     if (static_cast<unsigned>(phys) >= static_cast<unsigned>(a.num_blocks)) {
-      bad_blk |= key <= kmax;
+      bad_blk |= t * kKeys + sk <= kmax;
       phys = 0;
     }
-    const int64_t base = (static_cast<int64_t>(phys) * a.num_kv_heads + kvh) * run_elems + sc * 8;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t off = base + static_cast<int64_t>((key + j) & bmask) * kHead;
-      kr[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.k_cache) + off);
-      vr[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.v_cache) + off);
-    }
+    return (static_cast<int64_t>(phys) * a.num_kv_heads + kvh) * run_elems + sc * 8 +
+           static_cast<int64_t>((t * kKeys + sk) & bmask) * kHead;
   };
-  auto store = [&](int buf, const u32x4 (&kr)[2], const u32x4 (&vr)[2], int valid) {
+  auto issue_k = [&](int t, int phys, u32x4 (&kr)[2]) {
+    const int64_t off = tile_rows(t, phys);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      kr[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.k_cache) + off + j * kHead);
+  };
+  auto issue_v = [&](int t, int phys, u32x4 (&vr)[2], int& valid) {
+    const int key = t * kKeys + sk;
+    valid = (key <= kmax ? 1 : 0) | (key + 1 <= kmax ? 2 : 0);
+    const int64_t off = tile_rows(t, phys);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      vr[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.v_cache) + off + j * kHead);
+  };
+  auto store_k = [&](int buf, const u32x4 (&kr)[2]) {
     T* sk_buf = s_k + buf * kTileK;
+    *reinterpret_cast<u32x4*>(&sk_buf[sk * kKRow + sc * 8]) = kr[0];
+    *reinterpret_cast<u32x4*>(&sk_buf[(sk + 1) * kKRow + sc * 8]) = kr[1];
+  };
+  auto store_v = [&](int buf, const u32x4 (&vr)[2], int valid) {
     T* sv_buf = s_vt + buf * kTileV;
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
     const u32x4 v0 = (valid & 1) ? vr[0] : z, v1 = (valid & 2) ? vr[1] : z;
-    *reinterpret_cast<u32x4*>(&sk_buf[sk * kKRow + sc * 8]) = kr[0];
-    *reinterpret_cast<u32x4*>(&sk_buf[(sk + 1) * kKRow + sc * 8]) = kr[1];
     // V transposed: dims sc * 8 .. + 7, keys sk and sk + 1 side by side.
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t a0 = v0[w], a1 = v1[w];
+      // Byte permutes: low halves of the two keys' dwords, then high halves.
       const int d = sc * 8 + 2 * w;
-      *reinterpret_cast<uint32_t*>(&sv_buf[d * kVRow + sk]) = (a0 & 0xffffu) | (a1 << 16);
-      *reinterpret_cast<uint32_t*>(&sv_buf[(d + 1) * kVRow + sk]) = (a0 >> 16) | (a1 & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(&sv_buf[d * kVRow + sk]) = __builtin_amdgcn_perm(v1[w], v0[w], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&sv_buf[(d + 1) * kVRow + sk]) = __builtin_amdgcn_perm(v1[w], v0[w], 0x07060302u);
     }
   };
 
@@ -191,17 +202,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   float m_ref = -INFINITY;  // reference maximum of this lane's column (base 2)
   float l_part = 0.0f;      // sum of this lane's probabilities (its 16 keys of each tile)
 
-  auto compute = [&](int t, int buf) {
-    const T* sk_buf = s_k + buf * kTileK;
-    const T* sv_buf = s_vt + buf * kTileV;
-    const int t0 = t * kKeys;
-    // S^T for 32 keys x this wave's 32 columns.
+  // S^T of a tile (32 keys x this wave's 32 columns) from the K buffer kb.
+  auto scores = [&](const T* kb) -> f32x16 {
     f32x16 s = f32x16{};
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(&sk_buf[(lane % 32) * kKRow + 16 * sl + 8 * half]);
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(&kb[(lane % 32) * kKRow + 16 * sl + 8 * half]);
       s = M::mma(ka, qb[sl], s);
     }
+    return s;
+  };
+
+  // Softmax and PV of tile t, whose scores are in s, with V from the buffer vb.  The next
+  // tile's scores are computed meanwhile from the K buffer kb_next and left in s: their
+  // MFMAs do not depend on this tile's vector work, so the two interleave in the wave's
+  // instruction stream and the matrix cores run while the softmax does.
+  auto step = [&](int t, f32x16& s, const T* kb_next, const T* vb) {
+    const int t0 = t * kKeys;
     // Causal mask, only on tiles that reach past the wave's first position; lane holds
     // keys t0 + 8j + 4 half + i, j, i = 0..3.  (Columns past the chunk have pos >= L and
     // zero queries: they compute finite values that are never stored.)
@@ -219,13 +236,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // the column's other 16 keys
     const float c = a.scale_log2;
     const float tm = tmax * c;
-    if (tm > m_ref + kRescaleSlack) {
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - tm);  // 0 on the first tile
-      m_ref = tm;
+    // Rescale when any column of the wave needs it (rare after the first tiles); a branch
+    // the whole wave takes or skips, so that the 64 products are not paid on every tile.
+    const bool need = tm > m_ref + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - tm) : 1.0f;  // 0 on the first tile
+      m_ref = need ? tm : m_ref;
       l_part *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
+    const f32x16 s_next = scores(kb_next);
     // Probabilities exp2(s c - m), split into a 16-bit value and the 16-bit rounding of
     // the rest.  A column that has seen no key yet (possible in a later part of a split
     // range) keeps m = -inf: its masked scores must give 0, not -inf - -inf.
@@ -233,14 +254,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     uint32_t ph[8], pl[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -mr));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -mr));
-      l_part += p0 + p1;
-      const T h0 = static_cast<T>(p0), h1 = static_cast<T>(p1);
-      const T e0 = static_cast<T>(p0 - static_cast<float>(h0));
-      const T e1 = static_cast<T>(p1 - static_cast<float>(h1));
-      ph[r / 2] = pack2(h0, h1);
-      pl[r / 2] = pack2(e0, e1);
+      const f32x2 p = f32x2{__builtin_amdgcn_exp2f(fmaf(s[r], c, -mr)),
+                            __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -mr))};
+      l_part += p.x + p.y;
+      // Two probabilities per conversion (round to nearest even), then the remainders.
+      const T2 h = __builtin_convertvector(p, T2);
+      const f32x2 hf = __builtin_convertvector(h, f32x2);
+      const T2 e = __builtin_convertvector(f32x2{p.x - hf.x, p.y - hf.y}, T2);
+      ph[r / 2] = __builtin_bit_cast(uint32_t, h);
+      pl[r / 2] = __builtin_bit_cast(uint32_t, e);
     }
     // O^T += V^T P^T: MFMA q covers keys 16q .. 16q + 15; its B operand is this lane's
     // probabilities 8q .. 8q + 7, whose keys (in operand order) are 16q + 4 half + i and
@@ -251,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       const u32x4 bl = u32x4{pl[4 * q], pl[4 * q + 1], pl[4 * q + 2], pl[4 * q + 3]};
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const T* vrow = &sv_buf[(32 * dt + lane % 32) * kVRow + 16 * q + 4 * half];
+        const T* vrow = &vb[(32 * dt + lane % 32) * kVRow + 16 * q + 4 * half];
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
         const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
@@ -259,47 +281,72 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         o[dt] = M::mma(va, bl, o[dt]);
       }
     }
+    s = s_next;
   };
 
-  // Pipeline: tile t is computed from LDS while tile t + 1 waits in registers (to be
-  // stored into the other buffer) and tile t + 2's loads are in flight; block ids run
-  // one tile further ahead, issued before the data loads they precede.
-  u32x4 ka[2], va[2], kb[2], vb[2];
-  int ma, mb;
-  // Tile numbers below are relative to the part's first tile.
+  // Pipeline.  K runs one tile ahead of V: during step r (tile r of the part) the LDS
+  // holds K of tile r + 1 (buffer (r + 1) % 2, for the next scores) and V of tile r
+  // (buffer r % 2); the stores at the end of the step put K of tile r + 2 into buffer r % 2
+  // and V of tile r + 1 into buffer (r + 1) % 2, both last read in the step before.  The
+  // loads of a step's stores were issued at the top of the step before, into the other of
+  // two register sets, and block ids run one tile ahead of the K loads.  Every load is
+  // issued whatever the key: keys past kmax read an in-bounds row (K rows past it are
+  // masked through their scores, V rows zeroed when staged), so the loads in flight always
+  // number the same and the waits before the stores stay exact.
+  const T* kbuf0 = s_k;
+  const T* kbuf1 = s_k + kTileK;
+  const T* vbuf0 = s_vt;
+  const T* vbuf1 = s_vt + kTileV;
+  u32x4 kA[2], vA[2], kB[2], vB[2];
+  int mA, mB;
   const int id0 = tile_block(t_first);
   const int id1 = tile_block(t_first + 1);
-  issue(t_first, id0, ka, va, ma);
-  int id_next = tile_block(t_first + 2);
-  issue(t_first + 1, id1, kb, vb, mb);
-  store(0, ka, va, ma);
+  issue_k(t_first, id0, kA);
+  issue_v(t_first, id0, vA, mA);
+  issue_k(t_first + 1, id1, kB);
+  store_k(0, kA);
+  store_v(0, vA, mA);
+  store_k(1, kB);
   __syncthreads();
-  // Drain the prologue's loads once: the loop header then sees only its own back edge's
-  // loads in flight, and its waits stay as loose as the pipeline allows.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  // The scheduling barriers keep the phases in this order, so that the wait for a staged
-  // tile's loads sits at its store, after the compute, and not before the next loads.
-  // Pairs of tiles per trip with one exit test, so that the loop header is reached only
-  // from the prologue and from the end of a pair.
-  int id_a = id_next;  // block ids of tile t + 2 at the top of a pair
-  int t = 0;
-  for (; t + 1 < n_tiles; t += 2) {
-    const int id3 = tile_block(t_first + t + 3);
-    issue(t_first + t + 2, id_a, ka, va, ma);
+  f32x16 s = scores(kbuf0);
+  // Every wave has read K buffer 0 before the first step's stores overwrite it.
+  __syncthreads();
+  // The loads of the first step's stores, issued as a step issues them (a block id, then
+  // K, then V), so that the loop header sees the same loads in flight from both sides.
+  int id_v = tile_block(t_first + 2);  // block of the next V issue (tile r + 2)
+  int id_k = tile_block(t_first + 3);  // block of the next K issue (tile r + 3)
+  issue_k(t_first + 2, id_v, kA);
+  issue_v(t_first + 1, id1, vA, mA);
+  // Pairs of steps per trip with one exit test, so that the loop header is reached only
+  // from the prologue and from the end of a pair; the scheduling barriers keep the loads
+  // ahead of the step and the stores after it.
+  int r = 0;
+  for (; r + 1 < n_tiles; r += 2) {
+    int id_n = tile_block(t_first + r + 4);
+    issue_k(t_first + r + 3, id_k, kB);
+    issue_v(t_first + r + 2, id_v, vB, mB);
+    id_v = id_k;
+    id_k = id_n;
     __builtin_amdgcn_sched_barrier(0);
-    compute(t_first + t, 0);
+    step(t_first + r, s, kbuf1, vbuf0);
     __builtin_amdgcn_sched_barrier(0);
-    store(1, kb, vb, mb);
+    store_k(0, kA);
+    store_v(1, vA, mA);
     __syncthreads();
-    id_a = tile_block(t_first + t + 4);
-    issue(t_first + t + 3, id3, kb, vb, mb);
+    id_n = tile_block(t_first + r + 5);
+    issue_k(t_first + r + 4, id_k, kA);
+    issue_v(t_first + r + 3, id_v, vA, mA);
+    id_v = id_k;
+    id_k = id_n;
     __builtin_amdgcn_sched_barrier(0);
-    compute(t_first + t + 1, 1);
+    step(t_first + r + 1, s, kbuf0, vbuf1);
     __builtin_amdgcn_sched_barrier(0);
-    store(0, ka, va, ma);
+    store_k(1, kB);
+    store_v(0, vB, mB);
     __syncthreads();
   }
-  if (t < n_tiles) compute(t_first + t, 0);  // an odd tile count: the last tile is in buffer 0
+  // An odd tile count: the last step (its next scores, of a tile past the part, go unused).
+  if (r < n_tiles) step(t_first + r, s, kbuf1, vbuf0);
 
   // A block id outside the pool anywhere in the workgroup's keys makes every output NaN.
   bad_blk = __syncthreads_or(bad_blk);
