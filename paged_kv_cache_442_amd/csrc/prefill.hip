@@ -63,13 +63,6 @@ struct MmaF16 {
   }
 };
 
-// Two 16-bit values packed into a dword, low half first.
-template <class T>
-__device__ __forceinline__ uint32_t pack2(T lo, T hi) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
-}
-
 template <class M, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   using T = typename M::elem;
