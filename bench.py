@@ -1,9 +1,9 @@
 """Paged-attention decode benchmark on one MI355X.
 
 A step is one decode step of one layer over the whole batch: the newest token of
-every sequence is written into its slot (``pa_reshape_and_cache``), then
-``pa_decode`` runs its three kernels (the work plan, the per-partition attention, the
-log-sum-exp merge of partitions).
+every sequence is written into its slot and the decode runs over every context
+(``pa_cache_and_decode``: the cache write and the work plan in one launch, then the
+per-partition attention, then the log-sum-exp merge of partitions).
 Inputs (pool, tables, queries) are resident in HBM before timing starts.
 
 The JSON line reports:
@@ -279,8 +279,7 @@ def main():
 
     def steps():
         for i in range(n):
-            sess.write_new_tokens()
-            sess.decode_plan()
+            sess.cache_and_decode_plan()       # the cache write and the plan: one launch
             ev.record(2 * i, stream)
             sess.decode_partitions()
             ev.record(2 * i + 1, stream)
@@ -302,28 +301,36 @@ def main():
     # Outside the timed region: the other kernels' times (events around every kernel) and
     # the step time with no events inside the loop at all.
     nb = min(n, 20)
-    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nb)]
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nb)]
     for e in bev:
         e[0].record(stream)
         sess.write_new_tokens()
         e[1].record(stream)
         sess.decode_plan()
         e[2].record(stream)
-        sess.decode_partitions()
+        sess.cache_and_decode_plan()
         e[3].record(stream)
-        sess.decode_reduce()
+        sess.decode_partitions()
         e[4].record(stream)
+        sess.decode_reduce()
+        e[5].record(stream)
     torch.cuda.synchronize()
     write_ms = np.array([e[0].elapsed_time(e[1]) for e in bev])
     plan_ms = np.array([e[1].elapsed_time(e[2]) for e in bev])
-    red_ms = np.array([e[3].elapsed_time(e[4]) for e in bev])
-    u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    u0.record(stream)
-    for _ in range(n):
-        sess.step()
-    u1.record(stream)
-    torch.cuda.synchronize()
-    ms_step_plain = u0.elapsed_time(u1) / n
+    fused_ms = np.array([e[2].elapsed_time(e[3]) for e in bev])
+    red_ms = np.array([e[4].elapsed_time(e[5]) for e in bev])
+
+    def plain_ms(step):
+        u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        u0.record(stream)
+        for _ in range(n):
+            step()
+        u1.record(stream)
+        torch.cuda.synchronize()
+        return u0.elapsed_time(u1) / n
+
+    ms_step_plain = plain_ms(sess.step)
+    ms_step_separate = plain_ms(sess.step_separate)
 
     part_avg_s = float(part_ms.mean()) * 1e-3
     achieved = B / part_avg_s / 1e9
@@ -395,10 +402,12 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
         "ms_per_step_no_events": round(ms_step_plain, 5),
-        "kernel_ms": {"reshape_and_cache": round(float(write_ms.mean()), 5),
-                      "decode_plan": round(float(plan_ms.mean()), 5),
+        "ms_per_step_no_events_four_launches": round(ms_step_separate, 5),
+        "kernel_ms": {"cache_write_and_plan": round(float(fused_ms.mean()), 5),
                       "decode_partitions": round(float(part_ms.mean()), 5),
-                      "decode_reduce": round(float(red_ms.mean()), 5)},
+                      "decode_reduce": round(float(red_ms.mean()), 5),
+                      "reshape_and_cache_alone": round(float(write_ms.mean()), 5),
+                      "decode_plan_alone": round(float(plan_ms.mean()), 5)},
         "roofline": {
             "bound": "hbm",
             "kernel": "decode_partition_kernel",

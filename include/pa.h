@@ -353,6 +353,32 @@ int pa_decode_reduce(pa_pool* pool, int32_t layer, const void* q, int32_t num_se
                      int32_t partition_tokens, float* out, void* workspace,
                      int64_t workspace_bytes, void* stream);
 
+/* One decode step of one layer in three launches instead of four: pa_reshape_and_cache
+ *   of the new rows (k, v, slots, n_tokens exactly as there) followed by pa_decode
+ *   (every other argument exactly as there), with the cache write and the decode plan
+ *   sharing one launch.  Outputs, cache contents and errors are those of the two calls
+ *   made one after the other: the plan reads only context_lens, so it may run beside
+ *   the writes, and the attention kernels start after both.  The order is the pages':
+ *   the new token's K/V lands in a block allocated on demand, then the attention kernel
+ *   reads the whole context through the block table ("vLLM explained", PagedAttention
+ *   section, item 4, and its two implementation layers).
+ *   Arguments are checked before anything is launched: an error launches nothing.
+ * pa_cache_and_decode_plan is the first of the three launches alone (the write and
+ *   the plan); pa_decode_partitions and pa_decode_reduce with the same decode
+ *   arguments finish the step. */
+int pa_cache_and_decode_plan(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                             const int64_t* slots, int32_t n_tokens, const void* q,
+                             int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
+                             int32_t max_blocks, const int32_t* context_lens, int32_t max_context,
+                             float scale, int32_t partition_tokens, float* out, void* workspace,
+                             int64_t workspace_bytes, void* stream);
+int pa_cache_and_decode(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                        const int64_t* slots, int32_t n_tokens, const void* q, int32_t num_seqs,
+                        int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                        const int32_t* context_lens, int32_t max_context, float scale,
+                        int32_t partition_tokens, float* out, void* workspace,
+                        int64_t workspace_bytes, void* stream);
+
 /* Sliding-window decode: pa_decode in which sequence s attends only to its last
  *   `window` tokens, [max(0, L_s - window), L_s) ("vLLM explained", table of when KV may be
  *   overwritten: with a sliding-window model the KV outside the window can be dropped).

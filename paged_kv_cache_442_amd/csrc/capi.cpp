@@ -445,8 +445,9 @@ int pa_export_free_stack(const pa_pool* pool, int32_t* out, int32_t cap, int32_t
   return ok();
 }
 
-int pa_reshape_and_cache(pa_pool* pool, int32_t layer, const void* k, const void* v,
-                         const int64_t* slots, int32_t n_tokens, void* stream) {
+// Checks a cache write's arguments and fills `w`; n_tokens == 0 gives total_chunks 0.
+static int prepare_cache_write(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                        const int64_t* slots, int32_t n_tokens, pa::CacheWrite* w) {
   int st = check_device_pool(pool, layer);
   if (st) return st;
   if (n_tokens < 0) return fail(PA_E_INVAL, "n_tokens < 0");
@@ -454,27 +455,39 @@ int pa_reshape_and_cache(pa_pool* pool, int32_t layer, const void* k, const void
   if (row_bytes % 16 != 0)
     return fail(PA_E_UNSUPPORTED, "head_dim * element bytes = %lld is not a multiple of 16",
                 static_cast<long long>(row_bytes));
-  if (n_tokens == 0) return ok();
+  const bool fp8 = pool->desc.kv_dtype == PA_FP8_E4M3;
+  if (fp8 && pool->desc.head_dim != pa::kHeadDim)
+    return fail(PA_E_UNSUPPORTED, "FP8 cache writes need head_dim %d", pa::kHeadDim);
+  *w = pa::CacheWrite{};
+  if (n_tokens == 0) return PA_OK;
   if (!k || !v || !slots) return fail(PA_E_INVAL, "k, v and slots must be non-NULL");
   if (reinterpret_cast<uintptr_t>(k) % 16 || reinterpret_cast<uintptr_t>(v) % 16)
     return fail(PA_E_INVAL, "k and v must be 16-byte aligned");
   void *kc, *vc;
   pa_pool_layer_ptrs(pool, layer, &kc, &vc);
-  const int64_t num_slots = static_cast<int64_t>(pool->desc.num_blocks) * pool->desc.block_size;
-  if (pool->desc.kv_dtype == PA_FP8_E4M3) {
-    if (pool->desc.head_dim != pa::kHeadDim)
-      return fail(PA_E_UNSUPPORTED, "FP8 cache writes need head_dim %d", pa::kHeadDim);
-    return hip_status(pa::launch_reshape_and_cache_fp8(k, v, slots, kc, vc, n_tokens,
-                                                       pool->desc.num_kv_heads, pool->desc.block_size,
-                                                       num_slots, 1.0f / pool->k_scale[layer],
-                                                       1.0f / pool->v_scale[layer],
-                                                       static_cast<hipStream_t>(stream)),
-                      "pa_reshape_and_cache");
-  }
-  return hip_status(pa::launch_reshape_and_cache(k, v, slots, kc, vc, n_tokens, pool->desc.num_kv_heads,
-                                                 pool->desc.block_size, num_slots,
-                                                 static_cast<int32_t>(row_bytes),
-                                                 static_cast<hipStream_t>(stream)),
+  w->k = k;
+  w->v = v;
+  w->slots = slots;
+  w->k_cache = kc;
+  w->v_cache = vc;
+  w->row_chunks = static_cast<int32_t>(row_bytes / 16);
+  w->total_chunks = static_cast<int64_t>(n_tokens) * pool->desc.num_kv_heads * w->row_chunks;
+  w->num_slots = static_cast<int64_t>(pool->desc.num_blocks) * pool->desc.block_size;
+  w->num_kv_heads = pool->desc.num_kv_heads;
+  w->block_size = pool->desc.block_size;
+  w->fp8 = fp8 ? 1 : 0;
+  w->inv_k = 1.0f / pool->k_scale[layer];
+  w->inv_v = 1.0f / pool->v_scale[layer];
+  return PA_OK;
+}
+
+int pa_reshape_and_cache(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                         const int64_t* slots, int32_t n_tokens, void* stream) {
+  pa::CacheWrite w;
+  const int st = prepare_cache_write(pool, layer, k, v, slots, n_tokens, &w);
+  if (st) return st;
+  if (w.total_chunks == 0) return ok();
+  return hip_status(pa::launch_reshape_and_cache(w, static_cast<hipStream_t>(stream)),
                     "pa_reshape_and_cache");
 }
 
@@ -574,6 +587,47 @@ int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs, int
   int st = pa_decode_plan(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
                           context_lens, max_context, scale, partition_tokens, out, workspace,
                           workspace_bytes, stream);
+  if (st) return st;
+  st = pa_decode_partitions(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+                            context_lens, max_context, scale, partition_tokens, out, workspace,
+                            workspace_bytes, stream);
+  if (st) return st;
+  return pa_decode_reduce(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+                          context_lens, max_context, scale, partition_tokens, out, workspace,
+                          workspace_bytes, stream);
+}
+
+int pa_cache_and_decode_plan(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                             const int64_t* slots, int32_t n_tokens, const void* q,
+                             int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
+                             int32_t max_blocks, const int32_t* context_lens, int32_t max_context,
+                             float scale, int32_t partition_tokens, float* out, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  pa::CacheWrite w;
+  int st = prepare_cache_write(pool, layer, k, v, slots, n_tokens, &w);
+  if (st) return st;
+  DecodeCall c;
+  st = prepare_decode(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+                      context_lens, max_context, scale, partition_tokens, out, workspace,
+                      workspace_bytes, &c);
+  if (st) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c.args.num_seqs == 0) {
+    if (w.total_chunks == 0) return ok();
+    return hip_status(pa::launch_reshape_and_cache(w, s), "pa_cache_and_decode_plan");
+  }
+  return hip_status(pa::launch_cache_write_plan(w, c.args, s), "pa_cache_and_decode_plan");
+}
+
+int pa_cache_and_decode(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                        const int64_t* slots, int32_t n_tokens, const void* q, int32_t num_seqs,
+                        int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                        const int32_t* context_lens, int32_t max_context, float scale,
+                        int32_t partition_tokens, float* out, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
+  int st = pa_cache_and_decode_plan(pool, layer, k, v, slots, n_tokens, q, num_seqs, num_q_heads,
+                                    block_tables, max_blocks, context_lens, max_context, scale,
+                                    partition_tokens, out, workspace, workspace_bytes, stream);
   if (st) return st;
   st = pa_decode_partitions(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
                             context_lens, max_context, scale, partition_tokens, out, workspace,

@@ -820,7 +820,9 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* s_tmp, int* tota
   return base + incl - x;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeArgs a) {
+// The plan's body: one workgroup of kPlanThreads threads runs it, alone in
+// decode_plan_kernel or beside the cache writes in cache_write_plan_kernel.
+__device__ __forceinline__ void plan_work(const DecodeArgs& a) {
   // Partial items are listed largest first (bucketed by their number of tiles), so that
   // the smallest units are the last ones claimed and the persistent workgroups finish
   // together.  The order of items within a bucket is whatever the LDS counters give:
@@ -900,6 +902,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeA
   }
 }
 
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const DecodeArgs a) { plan_work(a); }
+
 // ------------------------------------------------------------------ decode reduce
 // Merges every multi-partition row from the partials the partition kernel left in the
 // workspace.  32 threads per (sequence, query head), four dims each.  (A merge inside the
@@ -925,23 +929,25 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeArgs a) 
 // One thread per 16-byte chunk of the new rows: token t, KV head h, chunk c goes to
 // block slot / bs, offset slot % bs of head h ("vLLM explained", PagedAttention
 // section, item 4: blocks fill on demand).
-__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
-    const u32x4* __restrict__ k, const u32x4* __restrict__ v, const int64_t* __restrict__ slots,
-    u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache, int64_t total_chunks,
-    int32_t num_kv_heads, int32_t block_size, int64_t num_slots, int32_t row_chunks) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= total_chunks) return;
-  const int64_t row = i / row_chunks;
-  const int c = static_cast<int>(i - row * row_chunks);
-  const int64_t t = row / num_kv_heads;
-  const int h = static_cast<int>(row - t * num_kv_heads);
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / block_size;
-  const int64_t off = slot - blk * block_size;
-  const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_chunks + c;
-  k_cache[dst] = k[i];
-  v_cache[dst] = v[i];
+__device__ __forceinline__ void write_row_chunk(const CacheWrite& w, int64_t i) {
+  if (i >= w.total_chunks) return;
+  const int64_t row = i / w.row_chunks;
+  const int c = static_cast<int>(i - row * w.row_chunks);
+  const int64_t t = row / w.num_kv_heads;
+  const int h = static_cast<int>(row - t * w.num_kv_heads);
+  const int64_t slot = w.slots[t];
+  if (slot < 0 || slot >= w.num_slots) return;
+  const int64_t blk = slot / w.block_size;
+  const int64_t off = slot - blk * w.block_size;
+  const int64_t dst = ((blk * w.num_kv_heads + h) * w.block_size + off) * w.row_chunks + c;
+  const u32x4* k = static_cast<const u32x4*>(w.k);
+  const u32x4* v = static_cast<const u32x4*>(w.v);
+  static_cast<u32x4*>(w.k_cache)[dst] = k[i];
+  static_cast<u32x4*>(w.v_cache)[dst] = v[i];
+}
+
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(const CacheWrite w) {
+  write_row_chunk(w, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
 }
 
 // FP8 cache writes: one thread per 16 stored bytes (16 elements) of a new row, read as
@@ -952,40 +958,60 @@ __device__ __forceinline__ float fp8_clamp(float y) {
   return y != y ? y : fminf(fmaxf(y, -448.0f), 448.0f);
 }
 
-__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
-    const u32x4* __restrict__ k, const u32x4* __restrict__ v, const int64_t* __restrict__ slots,
-    u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache, int64_t total_chunks,
-    int32_t num_kv_heads, int32_t block_size, int64_t num_slots, float inv_k, float inv_v) {
+__device__ __forceinline__ void write_row_chunk_fp8(const CacheWrite& w, int64_t i) {
   constexpr int kRowChunks = kHeadDim / 16;  // 16-byte chunks of a stored row
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= total_chunks) return;
+  if (i >= w.total_chunks) return;
   const int64_t row = i / kRowChunks;
   const int c = static_cast<int>(i - row * kRowChunks);
-  const int64_t t = row / num_kv_heads;
-  const int h = static_cast<int>(row - t * num_kv_heads);
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / block_size;
-  const int64_t off = slot - blk * block_size;
-  const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * kRowChunks + c;
+  const int64_t t = row / w.num_kv_heads;
+  const int h = static_cast<int>(row - t * w.num_kv_heads);
+  const int64_t slot = w.slots[t];
+  if (slot < 0 || slot >= w.num_slots) return;
+  const int64_t blk = slot / w.block_size;
+  const int64_t off = slot - blk * w.block_size;
+  const int64_t dst = ((blk * w.num_kv_heads + h) * w.block_size + off) * kRowChunks + c;
   auto quantize16 = [](u32x4 a0, u32x4 a1, float inv) -> u32x4 {
     u32x4 out;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const u32x4& a = w < 2 ? a0 : a1;
-      const uint32_t x0 = a[2 * (w % 2)], x1 = a[2 * (w % 2) + 1];
+    for (int q = 0; q < 4; ++q) {
+      const u32x4& a = q < 2 ? a0 : a1;
+      const uint32_t x0 = a[2 * (q % 2)], x1 = a[2 * (q % 2) + 1];
       const float e0 = fp8_clamp(__uint_as_float(x0 << 16) * inv);
       const float e1 = fp8_clamp(__uint_as_float(x0 & 0xffff0000u) * inv);
       const float e2 = fp8_clamp(__uint_as_float(x1 << 16) * inv);
       const float e3 = fp8_clamp(__uint_as_float(x1 & 0xffff0000u) * inv);
       int d = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
       d = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, d, true);
-      out[w] = static_cast<uint32_t>(d);
+      out[q] = static_cast<uint32_t>(d);
     }
     return out;
   };
-  k_cache[dst] = quantize16(k[2 * i], k[2 * i + 1], inv_k);
-  v_cache[dst] = quantize16(v[2 * i], v[2 * i + 1], inv_v);
+  const u32x4* k = static_cast<const u32x4*>(w.k);
+  const u32x4* v = static_cast<const u32x4*>(w.v);
+  static_cast<u32x4*>(w.k_cache)[dst] = quantize16(k[2 * i], k[2 * i + 1], w.inv_k);
+  static_cast<u32x4*>(w.v_cache)[dst] = quantize16(v[2 * i], v[2 * i + 1], w.inv_v);
+}
+
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(const CacheWrite w) {
+  write_row_chunk_fp8(w, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
+}
+
+// One launch for a decode step's first two stages: workgroup 0 lists the decode work
+// (plan_work), the others write the new rows into their slots.  The plan reads only the
+// context lengths, which the writes leave alone, and the partition kernel after this
+// launch sees both.
+template <bool FP8>
+__global__ __launch_bounds__(kPlanThreads) void cache_write_plan_kernel(const CacheWrite w,
+                                                                        const DecodeArgs a) {
+  if (blockIdx.x == 0) {
+    plan_work(a);
+    return;
+  }
+  const int64_t i = static_cast<int64_t>(blockIdx.x - 1) * blockDim.x + threadIdx.x;
+  if constexpr (FP8)
+    write_row_chunk_fp8(w, i);
+  else
+    write_row_chunk(w, i);
 }
 
 // ------------------------------------------------------------------ block copies
@@ -1108,34 +1134,24 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_reshape_and_cache(const void* k, const void* v, const int64_t* slots,
-                                    void* k_cache, void* v_cache, int32_t n_tokens,
-                                    int32_t num_kv_heads, int32_t block_size, int64_t num_slots,
-                                    int32_t row_bytes, hipStream_t s) {
+hipError_t launch_reshape_and_cache(const CacheWrite& w, hipStream_t s) {
   (void)hipGetLastError();
-  const int32_t row_chunks = row_bytes / 16;
-  const int64_t total = static_cast<int64_t>(n_tokens) * num_kv_heads * row_chunks;
-  if (total == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
-  hipLaunchKernelGGL(reshape_and_cache_kernel, grid, dim3(256), 0, s,
-                     static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), slots,
-                     static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), total,
-                     num_kv_heads, block_size, num_slots, row_chunks);
+  if (w.total_chunks == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((w.total_chunks + 255) / 256));
+  if (w.fp8)
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel, grid, dim3(256), 0, s, w);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_kernel, grid, dim3(256), 0, s, w);
   return hipGetLastError();
 }
 
-hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, const int64_t* slots,
-                                        void* k_cache, void* v_cache, int32_t n_tokens,
-                                        int32_t num_kv_heads, int32_t block_size, int64_t num_slots,
-                                        float inv_k, float inv_v, hipStream_t s) {
+hipError_t launch_cache_write_plan(const CacheWrite& w, const DecodeArgs& a, hipStream_t s) {
   (void)hipGetLastError();
-  const int64_t total = static_cast<int64_t>(n_tokens) * num_kv_heads * (kHeadDim / 16);
-  if (total == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
-  hipLaunchKernelGGL(reshape_and_cache_fp8_kernel, grid, dim3(256), 0, s,
-                     static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), slots,
-                     static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), total,
-                     num_kv_heads, block_size, num_slots, inv_k, inv_v);
+  const dim3 grid(static_cast<unsigned>(1 + (w.total_chunks + kPlanThreads - 1) / kPlanThreads));
+  if (w.fp8)
+    hipLaunchKernelGGL(cache_write_plan_kernel<true>, grid, dim3(kPlanThreads), 0, s, w, a);
+  else
+    hipLaunchKernelGGL(cache_write_plan_kernel<false>, grid, dim3(kPlanThreads), 0, s, w, a);
   return hipGetLastError();
 }
 

@@ -43,17 +43,25 @@ hipError_t launch_decode_plan(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_partitions(const DecodeArgs& a, int dtype, int group, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t s);
 
-hipError_t launch_reshape_and_cache(const void* k, const void* v, const int64_t* slots,
-                                    void* k_cache, void* v_cache, int32_t n_tokens,
-                                    int32_t num_kv_heads, int32_t block_size, int64_t num_slots,
-                                    int32_t row_bytes, hipStream_t s);
+// New K/V rows [n_tokens][num_kv_heads][head_dim] written to their slots of one layer.
+// A 16/32-bit pool copies the rows; an FP8 pool takes bf16 rows (head_dim 128) and
+// quantizes them with the float32 reciprocals inv_k, inv_v of the layer's scales.
+struct CacheWrite {
+  const void* k;
+  const void* v;
+  const int64_t* slots;     // [n_tokens]; -1 (or out of range) skips the token
+  void* k_cache;            // one layer: [N][Hkv][bs][head_dim]
+  void* v_cache;
+  int64_t total_chunks;     // 16-byte chunks of stored rows: n_tokens * Hkv * row_chunks
+  int64_t num_slots;        // N * bs
+  int32_t num_kv_heads, block_size, row_chunks;
+  int32_t fp8;              // 1: quantizing FP8 write
+  float inv_k, inv_v;
+};
 
-// FP8 cache writes from bf16 rows [n_tokens][num_kv_heads][128]; inv_k, inv_v are the
-// float32 reciprocals of the layer's scales.
-hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, const int64_t* slots,
-                                        void* k_cache, void* v_cache, int32_t n_tokens,
-                                        int32_t num_kv_heads, int32_t block_size, int64_t num_slots,
-                                        float inv_k, float inv_v, hipStream_t s);
+hipError_t launch_reshape_and_cache(const CacheWrite& w, hipStream_t s);
+// One launch that does the cache write and the decode plan (launch_decode_plan's work).
+hipError_t launch_cache_write_plan(const CacheWrite& w, const DecodeArgs& a, hipStream_t s);
 
 // base: pool base, holding `arrays` (= 2 * num_layers) arrays, each of num_blocks blocks of
 // block_bytes bytes (one layer's K or V part of a block).

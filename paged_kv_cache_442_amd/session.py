@@ -141,7 +141,19 @@ class DecodeSession:
                             self.max_context, self.scale, self.out, self.workspace,
                             self.partition_tokens, stream)
 
+    def cache_and_decode_plan(self, stream=None):
+        pa.pa_cache_and_decode_plan(self.pool, self.layer, self.new_k, self.new_v, self.new_slots,
+                                    self.q, self.tables, self.ctx, self.max_context, self.scale,
+                                    self.out, self.workspace, self.partition_tokens, stream)
+
     def step(self, stream=None):
+        """One decode step: the new tokens' cache write and the decode, in three launches."""
+        pa.pa_cache_and_decode(self.pool, self.layer, self.new_k, self.new_v, self.new_slots,
+                               self.q, self.tables, self.ctx, self.max_context, self.scale,
+                               self.out, self.workspace, self.partition_tokens, stream)
+
+    def step_separate(self, stream=None):
+        """The same step as ``pa_reshape_and_cache`` then ``pa_decode`` (four launches)."""
         self.write_new_tokens(stream)
         self.decode(stream)
 

@@ -139,6 +139,58 @@ def test_plan_partitions_reduce_equals_decode():
     assert torch.equal(one.view(torch.int32), sess.out.view(torch.int32))
 
 
+@pytest.mark.parametrize("dtype,H_q,H_kv,bs,part,fp8", [
+    (wl.F32, 8, 8, 16, 0, False), (wl.F16, 32, 32, 16, 64, False),
+    (wl.BF16, 64, 8, 16, 0, False), (wl.BF16, 32, 8, 32, 128, False),
+    (wl.BF16, 16, 8, 16, 0, True), (wl.BF16, 64, 8, 16, 0, True),
+])
+def test_cache_and_decode_equals_separate_calls(dtype, H_q, H_kv, bs, part, fp8):
+    """pa_cache_and_decode (write and plan in one launch) against pa_reshape_and_cache
+    then pa_decode on a second, identical pool: the same cache bytes and output bits."""
+    announce(f"cache_and_decode vs separate calls dtype={dtype} H_q={H_q} H_kv={H_kv} "
+             f"bs={bs} part={part} fp8={fp8}")
+    w = wl.custom_decode(200 + H_q + bs, dtype, EDGE_LENS + [0, 2048], H_q, H_kv, block_size=bs)
+    sep = DecodeSession(w, partition_tokens=part, cache_fp8=fp8)
+    sep.step_separate()
+    fused = DecodeSession(w, partition_tokens=part, cache_fp8=fp8)
+    fused.step()
+    torch.cuda.synchronize()
+    assert torch.equal(sep.storage, fused.storage)
+    assert torch.equal(sep.out.view(torch.int32), fused.out.view(torch.int32))
+    if not fp8:
+        check_against_oracle(fused, range(w.num_seqs))
+    # Only the write (no sequences to decode), then only the decode (no new rows).
+    fused.storage.copy_(sep.storage)
+    fused.out.fill_(7.0)
+    empty_q = fused.q[:0]
+    pa.pa_cache_and_decode(fused.pool, 0, fused.new_k, fused.new_v, fused.new_slots, empty_q,
+                           fused.tables[:0], fused.ctx[:0], 0, fused.scale, fused.out[:0],
+                           fused.workspace, part)
+    none = fused.new_slots[:0]
+    pa.pa_cache_and_decode(fused.pool, 0, fused.new_k[:0], fused.new_v[:0], none, fused.q,
+                           fused.tables, fused.ctx, fused.max_context, fused.scale, fused.out,
+                           fused.workspace, part)
+    torch.cuda.synchronize()
+    assert torch.equal(sep.storage, fused.storage)
+    assert torch.equal(sep.out.view(torch.int32), fused.out.view(torch.int32))
+
+
+def test_cache_and_decode_rejects_before_launching():
+    announce("cache_and_decode argument errors")
+    w = wl.custom_decode(11, wl.BF16, [40, 17], 8, 8, block_size=16)
+    sess = DecodeSession(w, partition_tokens=64)
+    sess.step_separate()
+    torch.cuda.synchronize()
+    before = sess.storage.clone()
+    bad_ws = sess.workspace[:16]               # too small for the decode
+    with pytest.raises(pa.PAError):
+        pa.pa_cache_and_decode(sess.pool, 0, sess.new_k, sess.new_v, sess.new_slots, sess.q,
+                               sess.tables, sess.ctx, sess.max_context, sess.scale, sess.out,
+                               bad_ws, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(before, sess.storage)
+
+
 def test_empty_and_invalid_sequences():
     announce("empty sequence, bad block id, bad length")
     w = wl.custom_decode(9, wl.BF16, [40, 40, 40, 40], 8, 8, block_size=16)
