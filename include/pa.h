@@ -431,7 +431,9 @@ int pa_seq_release_before(pa_pool* pool, int32_t seq, int32_t token, int32_t* n_
  * or the row range is read or written.  Rows not owned by any sequence are untouched.
  * Supported: head_dim 128; fp16 and bf16 caches (PA_E_UNSUPPORTED for fp32);
  * num_q_heads / num_kv_heads in {1, 2, 4, 8}; block_size a power of two >= 16; at most
- * 65535 sequences per call. */
+ * 65535 sequences per call, and at most 2^31 - 1 workgroups: ceil(max_query_len /
+ * (128 / group)) row blocks x ceil(max_context / 2048) key parts x num_seqs x
+ * num_kv_heads (PA_E_UNSUPPORTED beyond either). */
 int64_t pa_prefill_workspace_bytes(const pa_pool* pool, int32_t num_rows, int32_t num_q_heads,
                                    int32_t max_context);
 int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_rows,

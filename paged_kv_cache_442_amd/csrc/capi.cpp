@@ -691,6 +691,14 @@ int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_
       return fail(PA_E_INVAL, "q and out must be 16-byte aligned");
   if (num_seqs > 65535 || d.num_kv_heads > 65535)
     return fail(PA_E_UNSUPPORTED, "more than 65535 sequences or KV heads in one call");
+  {
+    const int64_t rows_per_block = pa::kPrefillColumns / group;
+    const int64_t workgroups = (max_query_len + rows_per_block - 1) / rows_per_block *
+                               prefill_pmax(max_context) * num_seqs * d.num_kv_heads;
+    if (workgroups > 0x7fffffff)
+      return fail(PA_E_UNSUPPORTED, "%lld workgroups (row blocks x key parts x sequences x KV "
+                  "heads) exceed 2^31 - 1", static_cast<long long>(workgroups));
+  }
   pa::PrefillArgs a;
   a.q = q;
   a.k_cache = pool->dev_base + static_cast<int64_t>(2 * layer) * pool->array_bytes;

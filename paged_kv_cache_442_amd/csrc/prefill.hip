@@ -35,7 +35,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kHead = 128;    // head_dim
 constexpr int kKeys = 32;     // keys per tile
-constexpr int kCols = 128;    // (row, head) columns per workgroup
+constexpr int kCols = kPrefillColumns;  // (row, head) columns per workgroup
 constexpr int kKRow = kHead + 8;   // K tile row stride in LDS (elements), against bank conflicts
 constexpr int kVRow = kKeys + 8;   // transposed V tile row stride (elements)
 constexpr float kRescaleSlack = 8.0f;
@@ -80,12 +80,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int half = lane / 32;  // which 8 of a 16-dim slice, which 4 keys of 8
-  const int seq = blockIdx.y;
-  const int kvh = blockIdx.z;
-  // blockIdx.x = (row block, part).  Row blocks go last to first: a chunk's last rows see
-  // the most keys, so the longest workgroups start first.
-  const int part = blockIdx.x % a.pmax;
-  const int r0 = (gridDim.x / a.pmax - 1 - blockIdx.x / a.pmax) * TR;
+  // Work order: w = (row block, part) + X * (sequence + S * KV head), X = gridDim.x,
+  // row blocks last to first (a chunk's last rows see the most keys, so a sequence's
+  // longest workgroups start first).  Consecutive workgroups of the grid go to the
+  // eight XCDs in turn, and each XCD has its own L2; the dispatch index is remapped so
+  // that XCD j runs the j-th eighth of the work order, i.e. whole (sequence, KV head)
+  // runs of row blocks, which read the same keys: those keys stay in that XCD's L2
+  // instead of being fetched into all eight.
+  const unsigned nwg = gridDim.x * gridDim.y * gridDim.z;
+  const unsigned bid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const unsigned xcd = bid % 8, xq = nwg / 8, xr = nwg % 8;
+  const unsigned w = (xcd < xr ? xcd * (xq + 1) : xr * (xq + 1) + (xcd - xr) * xq) + bid / 8;
+  const int wx = static_cast<int>(w % gridDim.x);
+  const int seq = static_cast<int>((w / gridDim.x) % gridDim.y);
+  const int kvh = static_cast<int>(w / gridDim.x / gridDim.y);
+  const int part = wx % a.pmax;
+  const int r0 = (static_cast<int>(gridDim.x) / a.pmax - 1 - wx / a.pmax) * TR;
 
   const int qs = a.query_start[seq];
   const int n_rows = a.query_start[seq + 1] - qs;

@@ -28,6 +28,10 @@ struct PrefillArgs {
   float* part_lse;            // [num_rows][Hq][pmax]
 };
 
+// (row, query head) columns per workgroup: 128 / group consecutive rows of one sequence
+// times the group's query heads.
+constexpr int kPrefillColumns = 128;
+
 // Keys per part of the split (64 tiles): long enough to amortize a part's start, short
 // enough that no single workgroup outlasts the batch.
 constexpr int kPrefillPartKeys = 2048;
