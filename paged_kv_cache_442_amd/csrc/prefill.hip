@@ -37,7 +37,12 @@ constexpr int kHead = 128;    // head_dim
 constexpr int kKeys = 32;     // keys per tile
 constexpr int kCols = kPrefillColumns;  // (row, head) columns per workgroup
 constexpr int kKRow = kHead + 8;   // K tile row stride in LDS (elements), against bank conflicts
-constexpr int kVRow = kKeys + 8;   // transposed V tile row stride (elements)
+// Transposed V tile row stride (elements): 18 dwords.  A staging store of a wave writes
+// 16 key pairs of 8 dims rows apart for each of its four 8-dim groups, 144 dwords apart:
+// 16 banks apart, so the 64 stores fill the banks twice over (at 20 dwords they were 160
+// apart and four-way conflicted).  The PV operand reads (8 bytes, 16 rows per pass) land
+// 18 dwords apart, on distinct bank pairs.
+constexpr int kVRow = kKeys + 4;
 constexpr float kRescaleSlack = 8.0f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -318,6 +323,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // K, then V), so that the loop header sees the same loads in flight from both sides.
   int id_v = tile_block(t_first + 2);  // block of the next V issue (tile r + 2)
   int id_k = tile_block(t_first + 3);  // block of the next K issue (tile r + 3)
+  // The id load stays ahead of the K/V loads, as in the loop: the loop header waits for
+  // that id alone only if it is the oldest load in flight on both of its entries
+  // (otherwise the wait there covers the K/V loads just issued, and they stop overlapping
+  // the step before their stores).
+  __builtin_amdgcn_sched_barrier(0);
   issue_k(t_first + 2, id_v, kA);
   issue_v(t_first + 1, id1, vA, mA);
   // Pairs of steps per trip with one exit test, so that the loop header is reached only
