@@ -53,6 +53,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
+// A load the compiler makes a scalar load: the address is the same for every lane and
+// the data is not written while the kernel runs.
+template <class X>
+__device__ __forceinline__ X ld_uniform(const X* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) X*)(p))[i];
+}
+
 struct MmaBF16 {
   typedef __bf16 elem;
   __device__ static f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
@@ -158,29 +165,53 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int sc = tid / 16;
   const int32_t* tbl = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
   const int64_t run_elems = static_cast<int64_t>(a.block_size) * kHead;
+  const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * run_elems;  // one block of the array
   const int sh = a.block_shift;
   const int bmask = a.block_size - 1;
-  bool bad_blk = false;
-  auto tile_block = [&](int t) -> int { return tbl[min(t * kKeys + sk, kmax) >> sh]; };
-  // Global address (elements) of this thread's two rows of tile t, given the tile's block.
-  auto tile_rows = [&](int t, int phys) -> int64_t {
-    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(a.num_blocks)) {
-      bad_blk |= t * kKeys + sk <= kmax;
-      phys = 0;
-    }
-    return (static_cast<int64_t>(phys) * a.num_kv_heads + kvh) * run_elems + sc * 8 +
-           static_cast<int64_t>((t * kKeys + sk) & bmask) * kHead;
+  // The block ids of a tile are the same for the whole workgroup: keys t0 .. t0 + 15 lie
+  // in the block of key t0 and keys t0 + 16 .. t0 + 31 in that of key t0 + 16 (the same
+  // block once blocks hold 32 keys or more), each clamped to kmax.  They are read with
+  // scalar loads, and a thread's element offset is one of the two scalar bases (its keys'
+  // half of the tile) plus a part that does not change from tile to tile.
+  const int64_t lane_off = sc * 8 + static_cast<int64_t>(sk & bmask) * kHead;
+  const bool upper_keys = sk >= kKeys / 2;
+  bool bad_blk = false;  // a block id outside the pool (wave-uniform)
+  struct TileBase {
+    int64_t lo, hi;  // element offsets of keys t0 .. t0 + 15 and t0 + 16 .. t0 + 31
   };
-  auto issue_k = [&](int t, int phys, u32x4 (&kr)[2]) {
-    const int64_t off = tile_rows(t, phys);
+  auto tile_block = [&](int t) -> TileBase {
+    const int t0 = t * kKeys;
+    int id0 = ld_uniform(tbl, min(t0, kmax) >> sh);
+    int id1 = ld_uniform(tbl, min(t0 + kKeys / 2, kmax) >> sh);
+    // Both keys are at most kmax, so both blocks hold keys this workgroup attends to.
+    if (static_cast<unsigned>(id0) >= static_cast<unsigned>(a.num_blocks)) {
+      bad_blk = true;
+      id0 = 0;
+    }
+    if (static_cast<unsigned>(id1) >= static_cast<unsigned>(a.num_blocks)) {
+      bad_blk = true;
+      id1 = 0;
+    }
+    const int64_t in_blk = static_cast<int64_t>(kvh) * run_elems + static_cast<int64_t>(t0 & bmask) * kHead;
+    return TileBase{id0 * blk_elems + in_blk, id1 * blk_elems + in_blk};
+  };
+  // Global address (elements) of this thread's first row of tile t.  The bases are
+  // copied to values first: a lane-dependent choice between two members of one object
+  // becomes a lane-dependent address into a private array (scratch memory).
+  auto tile_rows = [&](const TileBase b) -> int64_t {
+    const int64_t lo = b.lo, hi = b.hi;
+    return (upper_keys ? hi : lo) + lane_off;
+  };
+  auto issue_k = [&](const TileBase b, u32x4 (&kr)[2]) {
+    const int64_t off = tile_rows(b);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       kr[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.k_cache) + off + j * kHead);
   };
-  auto issue_v = [&](int t, int phys, u32x4 (&vr)[2], int& valid) {
+  auto issue_v = [&](int t, const TileBase b, u32x4 (&vr)[2], int& valid) {
     const int key = t * kKeys + sk;
     valid = (key <= kmax ? 1 : 0) | (key + 1 <= kmax ? 2 : 0);
-    const int64_t off = tile_rows(t, phys);
+    const int64_t off = tile_rows(b);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       vr[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.v_cache) + off + j * kHead);
@@ -241,7 +272,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     float tmax = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // the column's other 16 keys
+    {
+      // The column's other 16 keys sit in lane l ^ 32: swapping the wave's two halves in
+      // registers (no LDS round trip) gives each lane its own value and its partner's.
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                                       false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float c = a.scale_log2;
     const float tm = tmax * c;
     // Rescale when any column of the wave needs it (rare after the first tiles); a branch
@@ -307,11 +344,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const T* vbuf1 = s_vt + kTileV;
   u32x4 kA[2], vA[2], kB[2], vB[2];
   int mA, mB;
-  const int id0 = tile_block(t_first);
-  const int id1 = tile_block(t_first + 1);
-  issue_k(t_first, id0, kA);
+  const TileBase id0 = tile_block(t_first);
+  const TileBase id1 = tile_block(t_first + 1);
+  issue_k(id0, kA);
   issue_v(t_first, id0, vA, mA);
-  issue_k(t_first + 1, id1, kB);
+  issue_k(id1, kB);
   store_k(0, kA);
   store_v(0, vA, mA);
   store_k(1, kB);
@@ -319,24 +356,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   f32x16 s = scores(kbuf0);
   // Every wave has read K buffer 0 before the first step's stores overwrite it.
   __syncthreads();
-  // The loads of the first step's stores, issued as a step issues them (a block id, then
-  // K, then V), so that the loop header sees the same loads in flight from both sides.
-  int id_v = tile_block(t_first + 2);  // block of the next V issue (tile r + 2)
-  int id_k = tile_block(t_first + 3);  // block of the next K issue (tile r + 3)
-  // The id load stays ahead of the K/V loads, as in the loop: the loop header waits for
-  // that id alone only if it is the oldest load in flight on both of its entries
-  // (otherwise the wait there covers the K/V loads just issued, and they stop overlapping
-  // the step before their stores).
-  __builtin_amdgcn_sched_barrier(0);
-  issue_k(t_first + 2, id_v, kA);
+  // The loads of the first step's stores, and the block ids of the two tiles after them.
+  TileBase id_v = tile_block(t_first + 2);  // blocks of the next V issue (tile r + 2)
+  TileBase id_k = tile_block(t_first + 3);  // blocks of the next K issue (tile r + 3)
+  issue_k(id_v, kA);
   issue_v(t_first + 1, id1, vA, mA);
+  TileBase id_n = tile_block(t_first + 4);  // blocks of the K issue after next (tile r + 4)
   // Pairs of steps per trip with one exit test, so that the loop header is reached only
   // from the prologue and from the end of a pair; the scheduling barriers keep the loads
-  // ahead of the step and the stores after it.
+  // ahead of the step and the stores after it.  The block ids (scalar loads) are read
+  // after a step's stores: scalar and LDS results share one wait counter, so a scalar
+  // load in flight during the step would hold up its first LDS wait, while the stores'
+  // wait before the barrier is there anyway.
   int r = 0;
   for (; r + 1 < n_tiles; r += 2) {
-    int id_n = tile_block(t_first + r + 4);
-    issue_k(t_first + r + 3, id_k, kB);
+    issue_k(id_k, kB);
     issue_v(t_first + r + 2, id_v, vB, mB);
     id_v = id_k;
     id_k = id_n;
@@ -345,9 +379,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     store_k(0, kA);
     store_v(1, vA, mA);
-    __syncthreads();
     id_n = tile_block(t_first + r + 5);
-    issue_k(t_first + r + 4, id_k, kA);
+    __syncthreads();
+    issue_k(id_k, kA);
     issue_v(t_first + r + 3, id_v, vA, mA);
     id_v = id_k;
     id_k = id_n;
@@ -356,6 +390,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     store_k(1, kB);
     store_v(0, vB, mB);
+    id_n = tile_block(t_first + r + 6);
     __syncthreads();
   }
   // An odd tile count: the last step (its next scores, of a tile past the part, go unused).
