@@ -16,6 +16,11 @@ kernels must convert from 4 x 4 = 16 distinct registers (the faulty code used 4)
 MFMA accumulators there) gave wrong outputs at g = 8 on the GPU, and no cause was found
 in its code; the kernels stay in VGPRs.
 
+4. No kernel uses scratch (private) memory.  A lane-dependent choice between two members
+of one small object (the prefill kernel's two block bases of a tile) once became a
+lane-dependent address into a private array: scratch loads inside the tile loop, whose
+wait also held up the tile's K/V loads.
+
 The kernels are compiled to assembly with the library's own flags; hipcc is needed,
 not a GPU.
 """
@@ -150,3 +155,23 @@ def test_no_kernel_uses_agprs(asm, prefill_asm):
 def test_the_agpr_scan_sees_an_accumulator_copy():
     text = "\n".join(["  - .agpr_count:     4", "v_accvgpr_read_b32 v21, a3"])
     assert agpr_use(text) == (4, 1, 1)
+
+
+def scratch_use(asm):
+    """(largest private segment of any kernel, scratch instructions, kernels seen)."""
+    sizes = [int(m) for m in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)]
+    insts = sum(1 for t in instructions(asm) if t.startswith("scratch_") or
+                (t.startswith("buffer_") and "off, s[0:3]" in t))
+    return (max(sizes) if sizes else 0), insts, len(sizes)
+
+
+def test_no_kernel_uses_scratch(asm, prefill_asm):
+    for text in (asm, prefill_asm):
+        most, insts, n = scratch_use(text)
+        assert n > 0
+        assert most == 0 and insts == 0, (most, insts)
+
+
+def test_the_scratch_scan_sees_a_spill():
+    text = "\n".join(["    .private_segment_fixed_size: 16", "scratch_load_dwordx2 v[80:81], v182, off"])
+    assert scratch_use(text) == (16, 1, 1)
