@@ -422,20 +422,23 @@ int pa_seq_release_before(pa_pool* pool, int32_t seq, int32_t token, int32_t* n_
  *   out          device fp32 [num_rows][num_q_heads][head_dim]
  *   workspace    device, caller-owned, 256-byte aligned, at least
  *                pa_prefill_workspace_bytes(pool, num_rows, num_q_heads, max_context)
- *                bytes (may be NULL when that is 0, i.e. max_context <= 2048)
- * The keys of a long row range are split in parts of 2048 (each part its own workgroup,
- * so that no workgroup outlasts the batch); such rows are combined by a log-sum-exp merge
- * kernel on the same stream, with the parts' outputs kept in the workspace.
+ *                bytes (may be NULL when that is 0, i.e. max_context <= the part size)
+ * The keys of a long row range are split in parts of pa_prefill_part_keys() keys (2048;
+ * each part its own workgroup, so that no workgroup outlasts the batch); such rows are
+ * combined by a log-sum-exp merge kernel on the same stream, with the parts' outputs kept
+ * in the workspace.
  * A sequence with n_s > L_s, L_s > max_context or L_s > max_blocks * block_size, or whose
  * keys touch a table id outside [0, num_blocks), gets NaN rows; nothing outside the pool
  * or the row range is read or written.  Rows not owned by any sequence are untouched.
  * Supported: head_dim 128; fp16 and bf16 caches (PA_E_UNSUPPORTED for fp32);
  * num_q_heads / num_kv_heads in {1, 2, 4, 8}; block_size a power of two >= 16; at most
  * 65535 sequences per call, and at most 2^31 - 1 workgroups: ceil(max_query_len /
- * (128 / group)) row blocks x ceil(max_context / 2048) key parts x num_seqs x
+ * (128 / group)) row blocks x ceil(max_context / part size) key parts x num_seqs x
  * num_kv_heads (PA_E_UNSUPPORTED beyond either). */
 int64_t pa_prefill_workspace_bytes(const pa_pool* pool, int32_t num_rows, int32_t num_q_heads,
                                    int32_t max_context);
+/* Keys per part of pa_prefill_chunked's split (host only, no GPU call). */
+int32_t pa_prefill_part_keys(void);
 int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_rows,
                        int32_t num_q_heads, const int32_t* query_start, int32_t num_seqs,
                        const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,

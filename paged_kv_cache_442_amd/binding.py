@@ -70,6 +70,7 @@ _SIGNATURES = {
     "pa_cache_and_decode": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32] + _DECODE_ARGS[2:]),
     "pa_cache_and_decode_plan": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32] + _DECODE_ARGS[2:]),
     "pa_prefill_workspace_bytes": (_I64, [_P, _I32, _I32, _I32]),
+    "pa_prefill_part_keys": (_I32, []),
     "pa_prefill_chunked": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _I32,
                                           _I32, ctypes.c_float, _P, _P, _I64, _P]),
     "pa_decode_window": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _I32,
@@ -514,6 +515,10 @@ def pa_cache_and_decode_plan(pool, layer, k, v, slots, q, block_tables, context_
                              scale, out, workspace, partition_tokens=0, stream=None):
     _cache_and_decode(lib().pa_cache_and_decode_plan, pool, layer, k, v, slots, q, block_tables,
                       context_lens, max_context, scale, out, workspace, partition_tokens, stream)
+
+
+def pa_prefill_part_keys():
+    return _check(lib().pa_prefill_part_keys())
 
 
 def pa_prefill_workspace_bytes(pool, num_rows, num_q_heads, max_context):

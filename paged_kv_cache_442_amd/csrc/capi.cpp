@@ -638,6 +638,8 @@ int pa_cache_and_decode(pa_pool* pool, int32_t layer, const void* k, const void*
                           workspace_bytes, stream);
 }
 
+int32_t pa_prefill_part_keys(void) { return pa::kPrefillPartKeys; }
+
 static int64_t prefill_pmax(int32_t max_context) {
   return std::max<int64_t>(1, (static_cast<int64_t>(max_context) + pa::kPrefillPartKeys - 1) /
                                   pa::kPrefillPartKeys);

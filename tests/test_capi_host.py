@@ -243,11 +243,13 @@ def test_batch_append_is_all_or_nothing():
 
 def test_prefill_workspace_is_needed_only_past_one_part():
     pool = host_pool(8, 16)
-    assert pa.pa_prefill_workspace_bytes(pool, 100, 4, 2048) == 0
-    rows, heads, pmax = 100, 4, 3                      # 4097 keys: parts of 2048
+    P = pa.pa_prefill_part_keys()
+    assert P > 0 and P % 32 == 0                       # whole 32-key tiles
+    assert pa.pa_prefill_workspace_bytes(pool, 100, 4, P) == 0
+    rows, heads, pmax = 100, 4, 3                      # 2P + 1 keys: three parts
     items = rows * heads * pmax
     lse = -(-items * 4 // 256) * 256
-    assert pa.pa_prefill_workspace_bytes(pool, rows, heads, 4097) == lse + items * 128 * 4
+    assert pa.pa_prefill_workspace_bytes(pool, rows, heads, 2 * P + 1) == lse + items * 128 * 4
 
 
 def test_decode_default_partition():

@@ -75,11 +75,13 @@ def test_prefill_small_shapes_all_rows(dtype, H_q, H_kv, bs):
 
 @pytest.mark.parametrize("dtype,H_q,H_kv", [(wl.BF16, 32, 8), (wl.F16, 64, 8), (wl.BF16, 8, 8)])
 def test_prefill_split_into_parts_all_rows(dtype, H_q, H_kv):
-    """Contexts past 2048 keys are split into parts and merged; a chunk across position
-    2048 has rows that see no key of the second part."""
-    announce(f"prefill split parts dtype={dtype} H_q={H_q} H_kv={H_kv}")
-    w = wl.custom_chunked(300 + H_q, dtype, [2000, 2100, 4000, 1], [100, 40, 65, 30], [], H_q, H_kv,
-                          block_size=16)
+    """Contexts past the part size are split into parts and merged; a chunk across the
+    first part boundary has rows that see no key of the second part, and one across the
+    second boundary spans three parts."""
+    P = pa.pa_prefill_part_keys()
+    announce(f"prefill split parts (part {P}) dtype={dtype} H_q={H_q} H_kv={H_kv}")
+    w = wl.custom_chunked(300 + H_q, dtype, [P - 48, P + 52, 2 * P - 96, 1], [100, 40, 65, 30], [],
+                          H_q, H_kv, block_size=16)
     sess = PrefillSession(w)
     assert sess.workspace_c is not None
     sess.step()
@@ -174,8 +176,10 @@ def test_block_size_that_is_not_a_power_of_two_is_rejected():
 
 
 def test_prefill_over_a_long_prefix_merges_many_parts():
-    """A 16k-token prefix: each row's keys span 9 parts of 2048 (sampled rows)."""
-    announce("prefill over a 16384-token prefix (9 parts), bf16 32/8")
+    """A 16k-token prefix: each row's keys span several parts (nine at 2048 keys a part),
+    merged (sampled rows)."""
+    announce("prefill over a 16384-token prefix (%d parts), bf16 32/8"
+             % -(-16640 // pa.pa_prefill_part_keys()))
     w = wl.custom_chunked(411, wl.BF16, [16384, 3], [256, 20], [], 32, 8, block_size=32)
     sess = PrefillSession(w)
     sess.step()
