@@ -271,6 +271,23 @@ class PrefillSession:
         self.prefill(stream)
         self.decode(stream)
 
+    def step_overlapped(self, side_stream):
+        """The same step with the decode rows on ``side_stream`` (a default-priority
+        stream): both wait for the cache write, the prefill runs on the current stream,
+        and the current stream waits for the decode at the end.  The decode's persistent
+        workgroups then take the compute-unit slots the prefill's shorter workgroups leave
+        free (the two kernels read the pool only and write separate outputs)."""
+        main = torch.cuda.current_stream()
+        self.write_step_tokens()
+        written = torch.cuda.Event()
+        written.record(main)
+        side_stream.wait_event(written)
+        self.prefill()
+        self.decode(side_stream.cuda_stream)
+        decoded = torch.cuda.Event()
+        decoded.record(side_stream)
+        main.wait_event(decoded)
+
 
 
 class PrefixCacheSession:

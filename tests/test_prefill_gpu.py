@@ -89,6 +89,26 @@ def test_prefill_split_into_parts_all_rows(dtype, H_q, H_kv):
     check_chunks(sess, lambda i: range(int(w.chunk_lens[i])))
 
 
+def test_overlapped_step_equals_sequential_step():
+    """Decode rows on a second stream beside the prefill: the same output bits."""
+    announce("mixed step: decode on a side stream == sequential")
+    w = wl.custom_chunked(13, wl.BF16, [0, 700, 2100], [300, 64, 129], [1, 33, 2500, 4096], 32, 8,
+                          block_size=32)
+    sess = PrefillSession(w)
+    sess.step()
+    torch.cuda.synchronize()
+    seq_c, seq_d = sess.out_c.clone(), sess.out_d.clone()
+    sess.out_c.fill_(3.0)
+    sess.out_d.fill_(3.0)
+    side = torch.cuda.Stream()
+    for _ in range(3):
+        sess.step_overlapped(side)
+    torch.cuda.synchronize()
+    assert torch.equal(seq_c.view(torch.int32), sess.out_c.view(torch.int32))
+    assert torch.equal(seq_d.view(torch.int32), sess.out_d.view(torch.int32))
+    check_chunks(sess, lambda i: range(int(w.chunk_lens[i])))
+
+
 def test_prefill_single_rows_equal_the_decode_oracle():
     """A one-row chunk is a decode row: the same numbers as the oracle's decode."""
     announce("prefill with one-row chunks")
