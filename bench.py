@@ -413,6 +413,7 @@ def main():
         "tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
         "ms_per_step_no_events": round(ms_step_plain, 5),
         "ms_per_step_no_events_four_launches": round(ms_step_separate, 5),
+        "partition_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(part_ms, [10, 50, 90])],
         "kernel_ms": {"cache_write_and_plan": round(float(fused_ms.mean()), 5),
                       "decode_partitions": round(float(part_ms.mean()), 5),
                       "decode_reduce": round(float(red_ms.mean()), 5),
