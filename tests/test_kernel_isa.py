@@ -160,8 +160,7 @@ def test_the_agpr_scan_sees_an_accumulator_copy():
 def scratch_use(asm):
     """(largest private segment of any kernel, scratch instructions, kernels seen)."""
     sizes = [int(m) for m in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)]
-    insts = sum(1 for t in instructions(asm) if t.startswith("scratch_") or
-                (t.startswith("buffer_") and "off, s[0:3]" in t))
+    insts = sum(1 for t in instructions(asm) if t.startswith("scratch_"))
     return (max(sizes) if sizes else 0), insts, len(sizes)
 
 
