@@ -497,15 +497,15 @@ def main():
 
 
 def bench_window(args, torch, pa, sess, w, B, stream):
-    """Sliding-window decode: the step writes the new tokens, then one pa_decode_window
-    call (plan, partitions, merge); its time is the decode figure."""
+    """Sliding-window decode: a step is one pa_cache_and_decode_window call (the new
+    tokens' write with the plan, partitions, merge); its time is the decode figure."""
     import math as _m
     tables = sess.tables
     def decode():
-        pa.pa_decode_window(sess.pool, 0, sess.q, tables, sess.ctx, sess.max_context, args.window,
-                            sess.scale, sess.out, sess.workspace, sess.partition_tokens)
+        pa.pa_cache_and_decode_window(sess.pool, 0, sess.new_k, sess.new_v, sess.new_slots, sess.q,
+                                      tables, sess.ctx, sess.max_context, args.window, sess.scale,
+                                      sess.out, sess.workspace, sess.partition_tokens)
     for _ in range(args.warmup):
-        sess.write_new_tokens()
         decode()
     torch.cuda.synchronize()
     n = args.steps
@@ -514,7 +514,6 @@ def bench_window(args, torch, pa, sess, w, B, stream):
 
     def steps():
         for i in range(n):
-            sess.write_new_tokens()
             ev.record(2 * i, stream)
             decode()
             ev.record(2 * i + 1, stream)
@@ -550,7 +549,7 @@ def bench_window(args, torch, pa, sess, w, B, stream):
                    "partition_tokens": args.partition or pa.pa_decode_default_partition(sess.pool, w.num_q_heads)},
         "tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
         "kernel_ms": {"decode_window (plan + partitions + merge)": round(dec_ms, 5)},
-        "roofline": {"bound": "hbm", "kernel": "pa_decode_window", "achieved": round(achieved, 2),
+        "roofline": {"bound": "hbm", "kernel": "pa_cache_and_decode_window (write + plan, partitions, merge)", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None},
         "max_abs_err_sampled": worst, "cpu_baseline": None,

@@ -391,6 +391,19 @@ int pa_decode_window(pa_pool* pool, int32_t layer, const void* q, int32_t num_se
                      int32_t partition_tokens, float* out, void* workspace, int64_t workspace_bytes,
                      void* stream);
 
+/* pa_cache_and_decode_window: pa_cache_and_decode with the sliding window of
+ *   pa_decode_window: the new rows' cache write and the windowed decode in three launches
+ *   (the write and the plan share the first).  Outputs, cache contents and errors are
+ *   those of pa_reshape_and_cache followed by pa_decode_window with the same arguments;
+ *   an argument error launches nothing. */
+int pa_cache_and_decode_window(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                               const int64_t* slots, int32_t n_tokens, const void* q,
+                               int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
+                               int32_t max_blocks, const int32_t* context_lens,
+                               int32_t max_context, int32_t window, float scale,
+                               int32_t partition_tokens, float* out, void* workspace,
+                               int64_t workspace_bytes, void* stream);
+
 /* pa_seq_release_before: the sliding window of `seq` has moved past `token`: every block
  *   whose tokens all lie before `token` (block j with (j + 1) * block_size <= token),
  *   except the sequence's last block, loses this sequence's reference (going back on

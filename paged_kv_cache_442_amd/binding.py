@@ -69,6 +69,9 @@ _SIGNATURES = {
     "pa_decode_reduce": (ctypes.c_int, _DECODE_ARGS),
     "pa_cache_and_decode": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32] + _DECODE_ARGS[2:]),
     "pa_cache_and_decode_plan": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32] + _DECODE_ARGS[2:]),
+    "pa_cache_and_decode_window": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P,
+                                                  _I32, _P, _I32, _I32, ctypes.c_float, _I32, _P,
+                                                  _P, _I64, _P]),
     "pa_prefill_workspace_bytes": (_I64, [_P, _I32, _I32, _I32]),
     "pa_prefill_part_keys": (_I32, []),
     "pa_prefill_chunked": (ctypes.c_int, [_P, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _I32,
@@ -515,6 +518,25 @@ def pa_cache_and_decode_plan(pool, layer, k, v, slots, q, block_tables, context_
                              scale, out, workspace, partition_tokens=0, stream=None):
     _cache_and_decode(lib().pa_cache_and_decode_plan, pool, layer, k, v, slots, q, block_tables,
                       context_lens, max_context, scale, out, workspace, partition_tokens, stream)
+
+
+def pa_cache_and_decode_window(pool, layer, k, v, slots, q, block_tables, context_lens, max_context,
+                               window, scale, out, workspace, partition_tokens=0, stream=None):
+    """``pa_reshape_and_cache(k, v, slots)`` then ``pa_decode_window(q, ...)``, in three
+    launches."""
+    import torch
+    dt = torch_dtype(pool.desc.kv_dtype)
+    n = slots.numel()
+    if k.shape[0] != n or v.shape != k.shape:
+        raise ValueError("k, v and slots disagree on the token count")
+    S, H_q = q.shape[0], q.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_cache_and_decode_window(
+        pool.handle, layer, _dev(k, dt, "k"), _dev(v, dt, "v"), _dev(slots, torch.int64, "slots"), n,
+        _dev(q, dt, "q"), S, H_q, _dev(block_tables, torch.int32, "block_tables"),
+        block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens"), max_context, window,
+        float(scale), partition_tokens, _dev(out, torch.float32, "out"),
+        None if workspace is None else _dev(workspace, name="workspace"), ws_bytes, _stream(stream)))
 
 
 def pa_prefill_part_keys():

@@ -640,6 +640,35 @@ int pa_cache_and_decode(pa_pool* pool, int32_t layer, const void* k, const void*
 
 int32_t pa_prefill_part_keys(void) { return pa::kPrefillPartKeys; }
 
+int pa_cache_and_decode_window(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                               const int64_t* slots, int32_t n_tokens, const void* q,
+                               int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
+                               int32_t max_blocks, const int32_t* context_lens,
+                               int32_t max_context, int32_t window, float scale,
+                               int32_t partition_tokens, float* out, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
+  pa::CacheWrite w;
+  int st = prepare_cache_write(pool, layer, k, v, slots, n_tokens, &w);
+  if (st) return st;
+  DecodeCall c;
+  st = prepare_decode(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
+                      context_lens, max_context, scale, partition_tokens, out, workspace,
+                      workspace_bytes, &c, window);
+  if (st) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c.args.num_seqs == 0) {
+    if (w.total_chunks == 0) return ok();
+    return hip_status(pa::launch_reshape_and_cache(w, s), "pa_cache_and_decode_window");
+  }
+  st = hip_status(pa::launch_cache_write_plan(w, c.args, s), "pa_cache_and_decode_window (write, plan)");
+  if (st) return st;
+  st = hip_status(pa::launch_decode_partitions(c.args, static_cast<int>(pool->desc.kv_dtype), c.group, s),
+                  "pa_cache_and_decode_window (partitions)");
+  if (st) return st;
+  if (c.args.pmax <= 1) return ok();
+  return hip_status(pa::launch_decode_reduce(c.args, s), "pa_cache_and_decode_window (reduce)");
+}
+
 static int64_t prefill_pmax(int32_t max_context) {
   return std::max<int64_t>(1, (static_cast<int64_t>(max_context) + pa::kPrefillPartKeys - 1) /
                                   pa::kPrefillPartKeys);
