@@ -101,8 +101,13 @@ def test_llama3_70b_full_size_sampled():
     torch.cuda.synchronize()
     assert torch.isfinite(sess.out).all()
     check_against_oracle(sess, sample_seqs(w, 6, 1))
-    # Another partition size gives another (equally valid) summation order.
+    # The three-launch step's output is pa_decode's, bit for bit, over the same cache.
     first = sess.out.clone()
+    sess.out.fill_(7.0)
+    sess.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int32), sess.out.view(torch.int32))
+    # Another partition size gives another (equally valid) summation order.
     sess.partition_tokens = 256
     ws = pa.pa_decode_workspace_bytes(sess.pool, w.num_seqs, w.num_q_heads, sess.max_context, 256)
     sess.workspace = torch.empty(ws, dtype=torch.uint8, device="cuda")
