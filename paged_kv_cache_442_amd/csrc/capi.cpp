@@ -447,7 +447,7 @@ int pa_export_free_stack(const pa_pool* pool, int32_t* out, int32_t cap, int32_t
 
 // Checks a cache write's arguments and fills `w`; n_tokens == 0 gives total_chunks 0.
 static int prepare_cache_write(pa_pool* pool, int32_t layer, const void* k, const void* v,
-                        const int64_t* slots, int32_t n_tokens, pa::CacheWrite* w) {
+                               const int64_t* slots, int32_t n_tokens, pa::CacheWrite* w) {
   int st = check_device_pool(pool, layer);
   if (st) return st;
   if (n_tokens < 0) return fail(PA_E_INVAL, "n_tokens < 0");
@@ -597,56 +597,15 @@ int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs, int
                           workspace_bytes, stream);
 }
 
-int pa_cache_and_decode_plan(pa_pool* pool, int32_t layer, const void* k, const void* v,
-                             const int64_t* slots, int32_t n_tokens, const void* q,
-                             int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
-                             int32_t max_blocks, const int32_t* context_lens, int32_t max_context,
-                             float scale, int32_t partition_tokens, float* out, void* workspace,
-                             int64_t workspace_bytes, void* stream) {
-  pa::CacheWrite w;
-  int st = prepare_cache_write(pool, layer, k, v, slots, n_tokens, &w);
-  if (st) return st;
-  DecodeCall c;
-  st = prepare_decode(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
-                      context_lens, max_context, scale, partition_tokens, out, workspace,
-                      workspace_bytes, &c);
-  if (st) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (c.args.num_seqs == 0) {
-    if (w.total_chunks == 0) return ok();
-    return hip_status(pa::launch_reshape_and_cache(w, s), "pa_cache_and_decode_plan");
-  }
-  return hip_status(pa::launch_cache_write_plan(w, c.args, s), "pa_cache_and_decode_plan");
-}
-
-int pa_cache_and_decode(pa_pool* pool, int32_t layer, const void* k, const void* v,
-                        const int64_t* slots, int32_t n_tokens, const void* q, int32_t num_seqs,
-                        int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
-                        const int32_t* context_lens, int32_t max_context, float scale,
-                        int32_t partition_tokens, float* out, void* workspace,
-                        int64_t workspace_bytes, void* stream) {
-  int st = pa_cache_and_decode_plan(pool, layer, k, v, slots, n_tokens, q, num_seqs, num_q_heads,
-                                    block_tables, max_blocks, context_lens, max_context, scale,
-                                    partition_tokens, out, workspace, workspace_bytes, stream);
-  if (st) return st;
-  st = pa_decode_partitions(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
-                            context_lens, max_context, scale, partition_tokens, out, workspace,
-                            workspace_bytes, stream);
-  if (st) return st;
-  return pa_decode_reduce(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks,
-                          context_lens, max_context, scale, partition_tokens, out, workspace,
-                          workspace_bytes, stream);
-}
-
-int32_t pa_prefill_part_keys(void) { return pa::kPrefillPartKeys; }
-
-int pa_cache_and_decode_window(pa_pool* pool, int32_t layer, const void* k, const void* v,
-                               const int64_t* slots, int32_t n_tokens, const void* q,
-                               int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
-                               int32_t max_blocks, const int32_t* context_lens,
-                               int32_t max_context, int32_t window, float scale,
-                               int32_t partition_tokens, float* out, void* workspace,
-                               int64_t workspace_bytes, void* stream) {
+// The new rows' cache write and a decode step (window 0: all tokens): the write and the plan
+// in one launch, then the partitions and the merge unless plan_only.  Every argument is
+// checked before the first launch.
+static int cache_and_decode(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                            const int64_t* slots, int32_t n_tokens, const void* q, int32_t num_seqs,
+                            int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                            const int32_t* context_lens, int32_t max_context, int32_t window,
+                            float scale, int32_t partition_tokens, float* out, void* workspace,
+                            int64_t workspace_bytes, bool plan_only, const char* what, void* stream) {
   pa::CacheWrite w;
   int st = prepare_cache_write(pool, layer, k, v, slots, n_tokens, &w);
   if (st) return st;
@@ -658,16 +617,53 @@ int pa_cache_and_decode_window(pa_pool* pool, int32_t layer, const void* k, cons
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (c.args.num_seqs == 0) {
     if (w.total_chunks == 0) return ok();
-    return hip_status(pa::launch_reshape_and_cache(w, s), "pa_cache_and_decode_window");
+    return hip_status(pa::launch_reshape_and_cache(w, s), what);
   }
-  st = hip_status(pa::launch_cache_write_plan(w, c.args, s), "pa_cache_and_decode_window (write, plan)");
-  if (st) return st;
+  st = hip_status(pa::launch_cache_write_plan(w, c.args, s), what);
+  if (st || plan_only) return st;
   st = hip_status(pa::launch_decode_partitions(c.args, static_cast<int>(pool->desc.kv_dtype), c.group, s),
-                  "pa_cache_and_decode_window (partitions)");
+                  what);
   if (st) return st;
   if (c.args.pmax <= 1) return ok();
-  return hip_status(pa::launch_decode_reduce(c.args, s), "pa_cache_and_decode_window (reduce)");
+  return hip_status(pa::launch_decode_reduce(c.args, s), what);
 }
+
+int pa_cache_and_decode_plan(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                             const int64_t* slots, int32_t n_tokens, const void* q,
+                             int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
+                             int32_t max_blocks, const int32_t* context_lens, int32_t max_context,
+                             float scale, int32_t partition_tokens, float* out, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  return cache_and_decode(pool, layer, k, v, slots, n_tokens, q, num_seqs, num_q_heads, block_tables,
+                          max_blocks, context_lens, max_context, 0, scale, partition_tokens, out,
+                          workspace, workspace_bytes, true, "pa_cache_and_decode_plan", stream);
+}
+
+int pa_cache_and_decode(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                        const int64_t* slots, int32_t n_tokens, const void* q, int32_t num_seqs,
+                        int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
+                        const int32_t* context_lens, int32_t max_context, float scale,
+                        int32_t partition_tokens, float* out, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
+  return cache_and_decode(pool, layer, k, v, slots, n_tokens, q, num_seqs, num_q_heads, block_tables,
+                          max_blocks, context_lens, max_context, 0, scale, partition_tokens, out,
+                          workspace, workspace_bytes, false, "pa_cache_and_decode", stream);
+}
+
+int pa_cache_and_decode_window(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                               const int64_t* slots, int32_t n_tokens, const void* q,
+                               int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
+                               int32_t max_blocks, const int32_t* context_lens,
+                               int32_t max_context, int32_t window, float scale,
+                               int32_t partition_tokens, float* out, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
+  return cache_and_decode(pool, layer, k, v, slots, n_tokens, q, num_seqs, num_q_heads, block_tables,
+                          max_blocks, context_lens, max_context, window, scale, partition_tokens,
+                          out, workspace, workspace_bytes, false, "pa_cache_and_decode_window",
+                          stream);
+}
+
+int32_t pa_prefill_part_keys(void) { return pa::kPrefillPartKeys; }
 
 static int64_t prefill_pmax(int32_t max_context) {
   return std::max<int64_t>(1, (static_cast<int64_t>(max_context) + pa::kPrefillPartKeys - 1) /
