@@ -172,30 +172,34 @@ def test_window_decode_matches_the_oracle(dtype, H_q, H_kv, window, part):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("dtype,H_q,H_kv,window,part", [
-    (wl.BF16, 64, 8, 100, 0), (wl.F16, 16, 4, 1000, 128), (wl.F32, 8, 8, 48, 64),
+@pytest.mark.parametrize("dtype,H_q,H_kv,window,part,fp8", [
+    (wl.BF16, 64, 8, 100, 0, False), (wl.F16, 16, 4, 1000, 128, False),
+    (wl.F32, 8, 8, 48, 64, False), (wl.BF16, 64, 8, 300, 0, True), (wl.BF16, 16, 8, 2000, 0, True),
 ])
-def test_cache_and_decode_window_equals_separate_calls(dtype, H_q, H_kv, window, part):
+def test_cache_and_decode_window_equals_separate_calls(dtype, H_q, H_kv, window, part, fp8):
     """pa_cache_and_decode_window (write and plan in one launch) against
-    pa_reshape_and_cache then pa_decode_window on a second, identical pool."""
+    pa_reshape_and_cache then pa_decode_window on a second, identical pool (for the
+    16/32-bit caches also against the oracle)."""
     import torch
     from paged_kv_cache_442_amd.session import DecodeSession
-    print(f"\n[case] cache_and_decode_window dtype={dtype} {H_q}/{H_kv} window={window} part={part}",
-          flush=True)
+    print(f"\n[case] cache_and_decode_window dtype={dtype} {H_q}/{H_kv} window={window} part={part} "
+          f"fp8={fp8}", flush=True)
     sys.stdout.flush()
     w = wl.custom_decode(400 + window, dtype, [0, 1, 15, 16, 17, 100, 777, 3000], H_q, H_kv,
                          block_size=16)
-    sep = DecodeSession(w, partition_tokens=part)
+    sep = DecodeSession(w, partition_tokens=part, cache_fp8=fp8)
     sep.write_new_tokens()
     pa.pa_decode_window(sep.pool, 0, sep.q, sep.tables, sep.ctx, sep.max_context, window, sep.scale,
                         sep.out, sep.workspace, part)
-    fused = DecodeSession(w, partition_tokens=part)
+    fused = DecodeSession(w, partition_tokens=part, cache_fp8=fp8)
     pa.pa_cache_and_decode_window(fused.pool, 0, fused.new_k, fused.new_v, fused.new_slots, fused.q,
                                   fused.tables, fused.ctx, fused.max_context, window, fused.scale,
                                   fused.out, fused.workspace, part)
     torch.cuda.synchronize()
     assert torch.equal(sep.storage, fused.storage)
     assert torch.equal(sep.out.view(torch.int32), fused.out.view(torch.int32))
+    if fp8:
+        return
     lens = np.asarray(w.context_lens)
     got = fused.out.cpu().numpy().astype(np.float64)
     tol = 1e-5 if dtype == wl.F32 else 2e-3
