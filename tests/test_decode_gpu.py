@@ -216,6 +216,31 @@ def test_empty_and_invalid_sequences():
     assert torch.equal(out[3], sess.out[3])
 
 
+def test_cache_and_decode_with_empty_and_invalid_sequences():
+    """The three-launch step over an empty sequence, a table id outside the pool and a
+    length past max_context: zeros, NaNs, NaNs, and the other rows and the cache write as
+    the separate calls give them."""
+    announce("cache_and_decode: empty sequence, bad block id, bad length")
+    w = wl.custom_decode(19, wl.BF16, [40, 40, 40, 40, 700], 16, 4, block_size=16)
+    sep = DecodeSession(w, partition_tokens=64)
+    sep.step_separate()
+    fused = DecodeSession(w, partition_tokens=64)
+    tables = fused.tables.clone()
+    ctx = fused.ctx.clone()
+    ctx[0] = 0                                  # empty -> zeros
+    tables[1, 1] = w.num_blocks + 5             # id outside the pool -> NaN, never read
+    ctx[2] = fused.max_context + 1              # longer than max_context -> NaN
+    out = torch.full_like(fused.out, 7.0)
+    pa.pa_cache_and_decode(fused.pool, 0, fused.new_k, fused.new_v, fused.new_slots, fused.q, tables,
+                           ctx, fused.max_context, fused.scale, out, fused.workspace, 64)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0)
+    assert torch.isnan(out[1]).all()
+    assert torch.isnan(out[2]).all()
+    assert torch.equal(out[3:].view(torch.int32), sep.out[3:].view(torch.int32))
+    assert torch.equal(sep.storage, fused.storage)
+
+
 def test_reshape_and_cache_bit_exact():
     announce("reshape_and_cache bit-exact vs oracle")
     w = wl.custom_decode(10, wl.F16, [33, 1, 16, 90], 4, 2, block_size=16)
