@@ -11,10 +11,17 @@ own.  A bit cast of a vector element taken as an lvalue once made the compiler w
 element 0 four times.  A 16-token tile is 4 wave-wide loads of 4 rows, so the fp16
 kernels must convert from 4 x 4 = 16 distinct registers (the faulty code used 4).
 
-3. No kernel keeps values in the accumulation registers (AGPRs).  The one build that did
-(the decode kernel for groups of 8 compiled for three workgroups per CU, which moved the
-MFMA accumulators there) gave wrong outputs at g = 8 on the GPU, and no cause was found
-in its code; the kernels stay in VGPRs.
+3. No kernel keeps values in the accumulation registers (AGPRs), and no instruction reads
+an MFMA result before the MFMA has written it.  A read of an MFMA's destination needs
+independent instructions after the MFMA (8 wait states for the 16x16x32 forms, 12 for
+32x32x16: what the compiler itself pads a straight-line read with, checked below), and
+nothing in hardware enforces it: a read too soon returns the register's old value.  The
+one build that used AGPRs (the decode kernel for groups of 8 compiled for three
+workgroups per CU) read its QK accumulator with v_accvgpr_read three wait states after
+the last MFMA, on the branch that skips the claim of the next unit, so the scores came
+from the previous tile; it gave wrong outputs at g = 8 on the GPU.  The scan below walks
+every path from each MFMA (branches included) and finds that read in that build; it
+finds none in the kernels as built.
 
 4. No kernel uses scratch (private) memory.  A lane-dependent choice between two members
 of one small object (the prefill kernel's two block bases of a tile) once became a
@@ -174,3 +181,165 @@ def test_no_kernel_uses_scratch(asm, prefill_asm):
 def test_the_scratch_scan_sees_a_spill():
     text = "\n".join(["    .private_segment_fixed_size: 16", "scratch_load_dwordx2 v[80:81], v182, off"])
     assert scratch_use(text) == (16, 1, 1)
+
+
+# --------------------------------------------------------------------------- MFMA results
+# Wait states a read of an MFMA's destination must trail the MFMA by.
+MFMA_READ_WAITS = {"v_mfma_f32_16x16x32_bf16": 8, "v_mfma_f32_16x16x32_f16": 8,
+                   "v_mfma_f32_32x32x16_bf16": 12, "v_mfma_f32_32x32x16_f16": 12}
+_BRANCH = re.compile(r"^s_c?branch")
+_STORES = ("global_store", "buffer_store", "ds_write", "ds_store", "flat_store", "scratch_store")
+
+
+def vector_regs(tok):
+    """{(bank, index)} of a VGPR / AGPR operand such as v5, v[2:5], a3, a[0:3]."""
+    tok = tok.rstrip(",")
+    m = re.fullmatch(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.fullmatch(r"([va])(\d+)", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+def code_with_labels(body):
+    """(instructions, {label: index of the instruction after it}) of one kernel."""
+    ins, labels = [], {}
+    for line in body.split("\n"):
+        s = line.split(";")[0].strip()
+        if not s:
+            continue
+        if s.endswith(":"):
+            if s.startswith("."):
+                labels[s[:-1]] = len(ins)
+            continue
+        if not s.startswith("."):
+            ins.append(s)
+    return ins, labels
+
+
+def _reads(op, operands):
+    regs = operands if op.startswith(_STORES) else operands[1:]
+    return set().union(*[vector_regs(x) for x in regs]) if regs else set()
+
+
+def _writes(op, operands):
+    if op.startswith(_STORES) or op.startswith("s_") or not operands:
+        return set()
+    return vector_regs(operands[0])
+
+
+def mfma_read_hazards(body):
+    """[(mfma, reader, wait states)] for every path (fall-through and branch targets) on
+    which a non-MFMA instruction reads an MFMA's destination too soon.  A register
+    rewritten on the way no longer counts; MFMA-to-MFMA accumulation chains are left
+    to the hardware."""
+    ins, labels = code_with_labels(body)
+    bad = []
+    for i, line in enumerate(ins):
+        parts = line.split()
+        if parts[0] not in MFMA_READ_WAITS:
+            continue
+        need = MFMA_READ_WAITS[parts[0]]
+        seen = {}
+        stack = [(i + 1, 0, frozenset(vector_regs(parts[1])))]
+        while stack:
+            j, waits, live = stack.pop()
+            while j < len(ins) and waits < need and live:
+                if seen.get((j, live), 1 << 30) <= waits:
+                    break
+                seen[(j, live)] = waits
+                toks = ins[j].split()
+                op = toks[0]
+                if not op.startswith("v_mfma") and _reads(op, toks[1:]) & live:
+                    bad.append((line, ins[j], waits))
+                    break
+                live = live - _writes(op, toks[1:])
+                if op == "s_endpgm":
+                    break
+                waits += int(toks[1], 0) + 1 if op == "s_nop" else 1
+                if _BRANCH.match(op):
+                    if toks[1] in labels:
+                        stack.append((labels[toks[1]], waits, live))
+                    if op == "s_branch":
+                        break
+                j += 1
+    return bad
+
+
+def test_no_mfma_result_is_read_too_soon(asm, prefill_asm):
+    checked = 0
+    for text in (asm, prefill_asm):
+        for name, body in kernel_bodies(text, r".").items():
+            if "v_mfma" in body:
+                checked += 1
+                assert not mfma_read_hazards(body), (name, mfma_read_hazards(body)[:2])
+    assert checked >= 14  # 6 decode kernels on MFMA, 8 prefill kernels
+
+
+def test_mfma_read_waits_match_the_compilers_own_padding(tmp_path):
+    """The compiler pads a straight-line read of each MFMA form with exactly these waits."""
+    src = tmp_path / "mfma_read.hip"
+    forms = {"v_mfma_f32_16x16x32_bf16": ("4", "__bf16", "mfma_f32_16x16x32_bf16", 3),
+             "v_mfma_f32_16x16x32_f16": ("4", "_Float16", "mfma_f32_16x16x32_f16", 3),
+             "v_mfma_f32_32x32x16_bf16": ("16", "__bf16", "mfma_f32_32x32x16_bf16", 15),
+             "v_mfma_f32_32x32x16_f16": ("16", "_Float16", "mfma_f32_32x32x16_f16", 15)}
+    code = ["#include <hip/hip_runtime.h>"]
+    for k, (n, t, b, last) in enumerate(forms.values()):
+        code.append(
+            "__global__ void k%d(const %s* a, const %s* b, float* o) {"
+            " typedef %s x8 __attribute__((ext_vector_type(8)));"
+            " typedef float acc __attribute__((ext_vector_type(%s)));"
+            " acc c = {}; c = __builtin_amdgcn_%s(((const x8*)a)[threadIdx.x], ((const x8*)b)[threadIdx.x], c, 0, 0, 0);"
+            " o[threadIdx.x] = c[0] * 3.0f + c[%d]; }" % (k, t, t, t, n, b, last))
+    src.write_text("\n".join(code))
+    out = tmp_path / "mfma_read.s"
+    res = subprocess.run([build.hipcc(), "--offload-arch=gfx950", "-O3", "--cuda-device-only", "-S",
+                          str(src), "-o", str(out)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    found = {}
+    for body in kernel_bodies(out.read_text(), r".").values():
+        ins, _ = code_with_labels(body)
+        at = next(i for i, x in enumerate(ins) if x.startswith("v_mfma"))
+        waits, j = 0, at + 1
+        while not _reads(ins[j].split()[0], ins[j].split()[1:]) & vector_regs(ins[at].split()[1]):
+            waits += int(ins[j].split()[1], 0) + 1 if ins[j].startswith("s_nop") else 1
+            j += 1
+        found[ins[at].split()[0]] = waits
+    assert found == MFMA_READ_WAITS
+
+
+def test_the_mfma_scan_finds_the_read_of_the_agpr_build(tmp_path):
+    """The decode kernel for groups of 8 built for three workgroups per CU (accumulators
+    in AGPRs): the scan finds its too-early v_accvgpr_read, in the g = 8 kernels only."""
+    src = open(os.path.join(build.CSRC, "kernels.hip")).read()
+    kept = "return E::kBytes == 4 ? 2 : (GW >= 4 ? 2 : 4);"
+    assert kept in src
+    variant = tmp_path / "kernels.hip"
+    variant.write_text(src.replace(kept, "return E::kBytes == 4 ? 2 : (GW == 8 ? 3 : GW >= 4 ? 2 : 4);"))
+    out = tmp_path / "variant.s"
+    flags = [f for f in build.HIP_FLAGS if f not in ("-shared", "-fPIC")]
+    res = subprocess.run([build.hipcc()] + flags + ["--cuda-device-only", "-S", "-I", build.INCLUDE,
+                                                    "-I", build.CSRC, str(variant), "-o", str(out)],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    flagged = {}
+    for name, body in kernel_bodies(out.read_text(), r"decode_partition_kernel").items():
+        flagged[name] = mfma_read_hazards(body)
+    hit = {n for n, h in flagged.items() if h}
+    assert hit and all("Li8ELi1E" in n for n in hit), sorted(hit)
+    assert all(r.startswith("v_accvgpr_read") and w < 8 for n in hit for _, r, w in flagged[n])
+
+
+def test_the_mfma_scan_follows_branches():
+    body = "\n".join(["v_mfma_f32_16x16x32_bf16 v[2:5], v[6:9], v[10:13], 0",
+                      "s_cbranch_scc1 .LBB0_2",
+                      "s_nop 7",
+                      "v_add_f32_e32 v1, v2, v3",
+                      ".LBB0_2:",
+                      "v_mov_b32_e32 v2, 0",
+                      "v_add_f32_e32 v1, v3, v4",
+                      "v_add_f32_e32 v1, v5, v4"])
+    bad = mfma_read_hazards(body)
+    # Via the branch: v2 is rewritten before any read, v3 is read 2 wait states after
+    # (the branch and the move); the fall-through path waits 9 states.
+    assert [(r, w) for _, r, w in bad] == [("v_add_f32_e32 v1, v3, v4", 2)]
