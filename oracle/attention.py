@@ -144,6 +144,37 @@ def prefill_rows(dtype, q_bits, row_seq, row_pos, k_pool_bits, v_pool_bits, tabl
     return out
 
 
+def causal_chunk(dtype, q_bits, k_contig, v_contig, first_pos, scale):
+    """Causal attention of one chunk's consecutive query rows over their sequence.
+
+    ``q_bits [C][H_q][d]`` raw bits of the rows at absolute positions ``first_pos ..
+    first_pos + C - 1``; ``k_contig, v_contig`` float64 ``[L][num_kv_heads][d]`` with
+    ``L >= first_pos + C``.  Row ``r`` attends to tokens ``0 .. first_pos + r`` (the same
+    definition as ``prefill_rows``).  For each query head the scores of all rows come
+    from one matrix product (a library routine); tokens after a row's position get no
+    weight, and the rest is the two-pass softmax of ``attend``: ``m = max z``,
+    ``w = exp(z - m)``, ``out = sum (w / sum w) v``.  Returns float64 ``[C][H_q][d]``.
+    """
+    q = fpbits.decode(dtype, q_bits)
+    C, H_q, d = q.shape
+    H_kv = k_contig.shape[1]
+    g = H_q // H_kv
+    n = int(first_pos) + C                       # keys any row of the chunk can see
+    if k_contig.shape[0] < n:
+        raise ValueError("the chunk's rows lie past the end of the sequence")
+    pos = int(first_pos) + np.arange(C)
+    visible = np.arange(n)[None, :] <= pos[:, None]                     # [C][n]
+    out = np.zeros((C, H_q, d))
+    for k in range(H_kv):
+        keys, values = k_contig[:n, k, :], v_contig[:n, k, :]
+        for h in range(k * g, (k + 1) * g):
+            z = np.where(visible, (q[:, h, :] @ keys.T) * scale, -np.inf)
+            m = z.max(axis=1, keepdims=True)
+            w = np.exp(z - m)
+            out[:, h, :] = (w / w.sum(axis=1, keepdims=True)) @ values
+    return out
+
+
 def partition_stats(q, keys, values, scale):
     """Softmax statistics of one query vector over one subset of tokens.
 

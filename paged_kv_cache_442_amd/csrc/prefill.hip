@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   {
     const u32x4* qrow = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + out_row * kHead);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qb[s] = col_ok ? qrow[2 * s + half] : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < 8; ++s) qb[s] = col_ok ? (qrow[2 * s + half] & a.q_and) ^ a.q_xor : u32x4{0u, 0u, 0u, 0u};
   }
 
   // Largest key any column of the workgroup sees, and this part's tiles of 0 .. kmax.
@@ -268,7 +268,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         s[r] = key <= pos ? s[r] : -INFINITY;
       }
     }
-    // Maximum of the raw scores (the scale is positive, so it commutes), then base 2.
+    // Maximum of the raw scores (the score scale is positive: the sign of the caller's
+    // scale went into the queries), then base 2.
     float tmax = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);

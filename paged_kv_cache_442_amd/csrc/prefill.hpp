@@ -19,7 +19,12 @@ struct PrefillArgs {
   int32_t num_rows, num_seqs, num_q_heads, num_kv_heads, max_blocks, num_blocks, block_size;
   int32_t block_shift;        // log2(block_size): block sizes are powers of two here
   int32_t max_context;
-  float scale_log2;           // scale * log2(e)
+  float scale_log2;           // |scale| * log2(e), or log2(e) for a zero scale: always > 0
+  // Applied to every dword of the query rows as (q & q_and) ^ q_xor: a negative scale
+  // flips the queries' sign bits (scale q.k = |scale| (-q).k, exactly), a zero scale
+  // clears them (every score 0, as scale q.k = 0).  The kernel's masking and running
+  // maximum need a positive score scale.
+  uint32_t q_and, q_xor;
   // Split of long key ranges: a row block's keys go in parts of part_keys (a multiple of
   // the 32-key tile); with more than one part each part writes its normalized output and
   // base-2 log-sum-exp here, and the merge kernel combines them into `out`.

@@ -320,6 +320,88 @@ def test_prefill_rows_match_causal_sdpa():
     assert np.array_equal(got[chunk], dec[0])
 
 
+def _chunk_case(seed, dtype, L, first_pos, C, H_q, H_kv):
+    rng = np.random.default_rng(seed)
+    q_rows = wl.round_to_bits(rng.standard_normal((C, H_q, 128), dtype=np.float32), dtype)
+    kt = wl.round_to_bits(rng.standard_normal((L, H_kv, 128), dtype=np.float32), dtype)
+    vt = wl.round_to_bits(rng.standard_normal((L, H_kv, 128), dtype=np.float32), dtype)
+    return q_rows, kt, vt
+
+
+@pytest.mark.parametrize("dtype,L,first_pos,C,H_q,H_kv", [
+    (wl.BF16, 60, 23, 30, 8, 2), (wl.F16, 40, 0, 40, 4, 4), (wl.BF16, 33, 32, 1, 8, 1)])
+def test_causal_chunk_matches_causal_sdpa(dtype, L, first_pos, C, H_q, H_kv):
+    """All rows of a chunk at once against torch's causal SDPA in float64, and against
+    prefill_rows (the row-by-row form) on the same rows."""
+    q_rows, kt, vt = _chunk_case(17 + C, dtype, L, first_pos, C, H_q, H_kv)
+    scale = attention.default_scale(128)
+    kc, vc = fpbits.decode(dtype, kt), fpbits.decode(dtype, vt)
+    got = attention.causal_chunk(dtype, q_rows, kc, vc, first_pos, scale)
+    pos = first_pos + np.arange(C)
+    mask = np.arange(L)[None, :] <= pos[:, None]
+    want = sdpa_reference(fpbits.decode(dtype, q_rows).transpose(1, 0, 2), kc.transpose(1, 0, 2),
+                          vc.transpose(1, 0, 2), mask).transpose(1, 0, 2)
+    assert np.max(np.abs(got - want)) <= 1e-12
+    bs = 8
+    n = -(-L // bs)
+    k_pool = np.zeros((n, H_kv, bs, 128), kt.dtype)
+    v_pool = np.zeros_like(k_pool)
+    for t in range(L):
+        k_pool[t // bs, :, t % bs] = kt[t]
+        v_pool[t // bs, :, t % bs] = vt[t]
+    rows = attention.prefill_rows(dtype, q_rows, np.zeros(C, np.int64), pos, k_pool, v_pool,
+                                  np.arange(n, dtype=np.int32)[None], np.array([L]), bs, scale)
+    assert np.max(np.abs(got - rows)) <= 1e-12
+
+
+def test_causal_chunk_first_row_from_the_start_is_the_first_value():
+    """A row at position 0 sees one key: its output is that key's value, exactly."""
+    q_rows, kt, vt = _chunk_case(5, wl.BF16, 20, 0, 20, 4, 2)
+    got = attention.causal_chunk(wl.BF16, q_rows, fpbits.decode(wl.BF16, kt),
+                                 fpbits.decode(wl.BF16, vt), 0, attention.default_scale(128))
+    v0 = fpbits.decode(wl.BF16, vt[0])
+    assert np.array_equal(got[0], np.repeat(v0, 2, axis=0))
+
+
+def _mutant_causal_chunk_strict(dtype, q_bits, k_contig, v_contig, first_pos, scale):
+    """A row that does not see its own token (strict causal mask)."""
+    q = fpbits.decode(dtype, q_bits)
+    C, H_q, d = q.shape
+    g = H_q // k_contig.shape[1]
+    n = first_pos + C
+    visible = np.arange(n)[None, :] < (first_pos + np.arange(C))[:, None]
+    out = np.zeros((C, H_q, d))
+    with np.errstate(invalid="ignore"):
+        for h in range(H_q):
+            z = np.where(visible, (q[:, h, :] @ k_contig[:n, h // g, :].T) * scale, -np.inf)
+            w = np.exp(z - z.max(axis=1, keepdims=True))
+            out[:, h, :] = (w / w.sum(axis=1, keepdims=True)) @ v_contig[:n, h // g, :]
+    return out
+
+
+def _mutant_causal_chunk_unscaled(dtype, q_bits, k_contig, v_contig, first_pos, scale):
+    return _ORIG_CAUSAL_CHUNK(dtype, q_bits, k_contig, v_contig, first_pos, 1.0)
+
+
+@pytest.mark.parametrize("mutant", [_mutant_causal_chunk_strict, _mutant_causal_chunk_unscaled])
+def test_causal_chunk_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(attention, "causal_chunk", mutant)
+    failed = 0
+    for case in [(wl.BF16, 60, 23, 30, 8, 2), (wl.F16, 40, 0, 40, 4, 4)]:
+        try:
+            test_causal_chunk_matches_causal_sdpa(*case)
+        except AssertionError:
+            failed += 1
+    try:
+        test_causal_chunk_first_row_from_the_start_is_the_first_value()
+    except AssertionError:
+        failed += 1
+    assert failed > 0
+
+
+_ORIG_CAUSAL_CHUNK = attention.causal_chunk
+
+
 # --------------------------------------------------------------------------- cache ops
 def test_reshape_and_cache_round_trip():
     w = wl.custom_decode(13, wl.F16, [20, 3], 4, 4, block_size=16)
