@@ -269,7 +269,8 @@ int pa_swap_blocks(pa_pool* pool, void* host_base, int64_t host_bytes, const int
  *   `layer` (a bit copy).  k, v: device [n_tokens][num_kv_heads][head_dim] in the
  *   pool's dtype, contiguous.  slots: device int64 [n_tokens]; slot s goes to block
  *   s / block_size, offset s % block_size; -1 means "skip this token".  Slots must be
- *   distinct (two tokens writing one slot race).  Slots outside [0, num_blocks *
+ *   distinct (two tokens writing one slot race; pa_check_slots checks, and the debug
+ *   build returns PA_E_INVAL before launching).  Slots outside [0, num_blocks *
  *   block_size) are skipped like -1, never written.  Blocks are filled on demand,
  *   token by token ("vLLM explained", PagedAttention section, item 4; carlstack page,
  *   section 三.1 figure: logical block 2 is placed in a block allocated on demand).
@@ -281,8 +282,9 @@ int pa_reshape_and_cache(pa_pool* pool, int32_t layer, const void* k, const void
  *   (device int32 [n_pairs][2]), block dst <- block src in every layer, K and V, all
  *   slots (carlstack page, section 三.2 and Fig. 1: copy only when a branch writes a
  *   different token).  The pairs run concurrently, so no dst may appear twice or also
- *   appear as a src (pairs from one step of the manager satisfy this).  Pairs with an
- *   id outside [0, num_blocks) are skipped. */
+ *   appear as a src (pairs from one step of the manager satisfy this; pa_check_copy_pairs
+ *   checks, and the debug build returns PA_E_INVAL before launching).  Pairs with an id
+ *   outside [0, num_blocks) are skipped. */
 int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* stream);
 
 /* Paged-attention decode of one layer: for each sequence s and query head h,
@@ -314,7 +316,7 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
  *                block are never read
  *   context_lens device int32 [num_seqs], 0 <= context_lens[s] <= max_context
  *   max_context  host bound on context_lens (sizes the grid and the workspace)
- *   scale        softmax scale, usually 1/sqrt(head_dim)
+ *   scale        softmax scale, any finite value (usually 1/sqrt(head_dim))
  *   out          device fp32 [num_seqs][num_q_heads][head_dim]; an empty sequence
  *                gets zeros
  *   workspace    device scratch of at least pa_decode_workspace_bytes(...) bytes,
@@ -432,6 +434,9 @@ int pa_seq_release_before(pa_pool* pool, int32_t seq, int32_t token, int32_t* n_
  *   context_lens device int32 [num_seqs]
  *   max_context  host bound on context_lens
  *   max_query_len host bound on every n_s (sizes the grid: rows past it are not computed)
+ *   scale        softmax scale, any finite value (usually 1/sqrt(head_dim)); a negative
+ *                scale is applied exactly (the kernel flips the queries' sign bits and
+ *                scales by |scale|), a zero scale gives every visible key equal weight
  *   out          device fp32 [num_rows][num_q_heads][head_dim]
  *   workspace    device, caller-owned, 256-byte aligned, at least
  *                pa_prefill_workspace_bytes(pool, num_rows, num_q_heads, max_context)
@@ -457,6 +462,22 @@ int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_
                        const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
                        int32_t max_context, int32_t max_query_len, float scale, float* out,
                        void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Precondition checks of the device calls, on host arrays (host only, no GPU call).
+ *   pa_check_slots: the slots of one pa_reshape_and_cache (or pa_cache_and_decode*) call
+ *   are distinct; slots outside [0, num_slots) are skipped by the kernels and not checked.
+ *   pa_check_copy_pairs: the (src, dst) pairs [n_pairs][2] of one pa_copy_blocks call
+ *   have distinct destinations, none of which is also a source; pairs with an id outside
+ *   [0, num_blocks) are skipped by the kernel and not checked.
+ *   PA_OK, or PA_E_INVAL with a message naming the offending slot or block.  Callers for
+ *   whom such a mistake would otherwise go unseen (the writes would race) use them, and
+ *   the library's debug build (libpa_debug.so, compiled with PA_DEBUG) runs them inside
+ *   those device calls on host copies of the arrays (the call then waits for `stream`),
+ *   returning PA_E_INVAL before anything is launched.
+ * pa_debug_build: 1 in the debug build, 0 otherwise. */
+int pa_check_slots(const int64_t* slots, int32_t n_tokens, int64_t num_slots);
+int pa_check_copy_pairs(const int32_t* pairs, int32_t n_pairs, int32_t num_blocks);
+int32_t pa_debug_build(void);
 
 /* Thread-local message of the last failed call on this thread ("" if none). */
 const char* pa_last_error(void);

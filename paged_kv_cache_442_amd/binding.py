@@ -6,6 +6,7 @@ become numpy buffers.  Every step of the computation runs in the library; if the
 library is missing the first call raises, there is no fallback.
 """
 
+import contextlib
 import ctypes
 import os
 
@@ -18,6 +19,9 @@ PA_OK, PA_E_INVAL, PA_E_NOMEM, PA_E_HIP, PA_E_UNSUPPORTED, PA_E_RANGE = 0, -1, -
 # PA_LIB_PATH selects another build of the same library (the default is the in-tree one).
 LIB_PATH = os.environ.get("PA_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "libpa.so")
+# The debug build: the same library with the caller's slot and copy-pair preconditions
+# checked before each launch.
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa_debug.so")
 
 _lib = None
 
@@ -94,23 +98,46 @@ _SIGNATURES = {
     "pa_host_block_refcount": (ctypes.c_int, [_P, _I32, _PI32]),
     "pa_export_host_free_stack": (ctypes.c_int, [_P, _PI32, _I32, _PI32]),
     "pa_swap_blocks": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _I32, _P]),
+    "pa_check_slots": (ctypes.c_int, [_PI64, _I32, _I64]),
+    "pa_check_copy_pairs": (ctypes.c_int, [_PI32, _I32, _I32]),
+    "pa_debug_build": (_I32, []),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 
 
+def bind(path):
+    """A ctypes handle on the build of the library at ``path``, every prototype set;
+    raises if it has not been built."""
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built; run __graft_entry__.build()" % path)
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
 def lib():
-    """Load ``libpa.so`` (once); raises if it has not been built."""
+    """The library every call below goes to: ``libpa.so``, loaded once (or the build
+    selected by ``using_library``)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError("libpa.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = handle
+        _lib = bind(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def using_library(path):
+    """Route the calls made inside the block to another build of the library (e.g. the
+    debug build); pools created there are freed by the build that created them."""
+    global _lib
+    saved = lib()
+    _lib = bind(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
 
 
 def _check(rc):
@@ -158,6 +185,7 @@ class Pool:
         self.handle = handle
         self.desc = desc
         self.storage = storage
+        self.owner = lib()  # the build that created the pool frees it
 
     @property
     def num_blocks(self):
@@ -168,8 +196,8 @@ class Pool:
         return self.desc.block_size
 
     def __del__(self):
-        if getattr(self, "handle", None) and _lib is not None:
-            _lib.pa_free_pool(self.handle)
+        if getattr(self, "handle", None) and getattr(self, "owner", None) is not None:
+            self.owner.pa_free_pool(self.handle)
             self.handle = None
 
 
@@ -206,8 +234,27 @@ def pa_alloc_pool(desc, storage=None, initial_free_order=None):
 
 def pa_free_pool(pool):
     if pool.handle:
-        _check(lib().pa_free_pool(pool.handle))
+        _check(pool.owner.pa_free_pool(pool.handle))
         pool.handle = None
+
+
+def pa_debug_build():
+    return int(lib().pa_debug_build())
+
+
+def pa_check_slots(slots, num_slots):
+    """Host check that the slots of one cache write are distinct (raises PAError)."""
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    buf = slots if len(slots) else np.zeros(1, np.int64)
+    _check(lib().pa_check_slots(buf.ctypes.data_as(_PI64), len(slots), int(num_slots)))
+
+
+def pa_check_copy_pairs(pairs, num_blocks):
+    """Host check of one copy call's (src, dst) pairs: distinct destinations, none also a
+    source (raises PAError)."""
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    buf = pairs if len(pairs) else np.zeros((1, 2), np.int32)
+    _check(lib().pa_check_copy_pairs(_i32p(buf), len(pairs), int(num_blocks)))
 
 
 def pa_pool_layer_ptrs(pool, layer):

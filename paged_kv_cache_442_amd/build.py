@@ -1,21 +1,27 @@
-"""Build ``libpa.so`` in-tree with hipcc for gfx950.
+"""Build ``libpa.so`` and its debug twin ``libpa_debug.so`` in-tree with hipcc for gfx950.
 
 ``python -m paged_kv_cache_442_amd.build`` (or ``build_library()``) always recompiles.
-The library is written next to this file; the ctypes binding loads it from there.
+Each source is compiled once to an object (in parallel); the C-ABI layer is compiled
+twice, the second time with ``-DPA_DEBUG`` (host-side precondition checks of the
+caller's slots and copy pairs before each launch), and the two libraries are linked
+from those objects.  Both are written next to this file; the ctypes binding loads
+``libpa.so`` from there.
 """
 
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libpa.so")
+DEBUG_LIB_PATH = os.path.join(HERE, "libpa_debug.so")
 
-SOURCES = ["capi.cpp", "block_manager.cpp", "kernels.hip", "prefill.hip"]
+SOURCES = ["capi.cpp", "block_manager.cpp", "preconditions.cpp", "kernels.hip", "prefill.hip"]
 
 # Packed-FP32 VALU forms are kept out of the generated code on purpose; the host
 # pass warns that it does not know the feature, which is harmless.
@@ -36,22 +42,46 @@ def hipcc():
     return path
 
 
+def _run_all(cmds, verbose):
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+    errors = []
+    for cmd, p in zip(cmds, procs):
+        out, err = p.communicate()
+        if p.returncode != 0:
+            errors.append("%s failed (%d):\n%s\n%s" % (" ".join(cmd[-3:]), p.returncode, out, err))
+        noise = [ln for ln in err.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+        if verbose and noise:
+            print("\n".join(noise), file=sys.stderr)
+    if errors:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+
+
 def build_library(verbose=False):
-    """Compile every source into ``libpa.so`` (atomically replaced); returns its path."""
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC] + \
-        [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
-        raise RuntimeError("hipcc failed (%d):\n%s\n%s" % (res.returncode, res.stdout, res.stderr))
-    noise = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
-    if verbose and noise:
-        print("\n".join(noise), file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
+    """Compile every source and link ``libpa.so`` and ``libpa_debug.so`` (each atomically
+    replaced); returns the path of ``libpa.so``."""
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
+        objs, cmds = {}, []
+        for src in SOURCES + ["capi.cpp#debug"]:
+            name, _, variant = src.partition("#")
+            obj = os.path.join(tmp, name.replace(".", "_") + ("_debug" if variant else "") + ".o")
+            extra = ["-DPA_DEBUG"] if variant else []
+            cmds.append([hipcc()] + compile_flags + extra + ["-I", INCLUDE, "-I", CSRC, "-c",
+                                                            os.path.join(CSRC, name), "-o", obj])
+            objs[src] = obj
+        _run_all(cmds, verbose)
+        links = []
+        for path, capi in ((LIB_PATH, "capi.cpp"), (DEBUG_LIB_PATH, "capi.cpp#debug")):
+            members = [objs[capi]] + [objs[s] for s in SOURCES if s != "capi.cpp"]
+            links.append([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + members +
+                         ["-o", path + ".tmp%d" % os.getpid()])
+        _run_all(links, verbose)
+        for path in (LIB_PATH, DEBUG_LIB_PATH):
+            os.replace(path + ".tmp%d" % os.getpid(), path)
     return LIB_PATH
 
 

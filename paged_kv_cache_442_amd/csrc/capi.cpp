@@ -16,6 +16,16 @@
 #include "block_manager.hpp"
 #include "kernels.hpp"
 #include "prefill.hpp"
+#include "preconditions.hpp"
+
+// The debug build (-DPA_DEBUG, libpa_debug.so) checks the caller's slot and copy-pair
+// preconditions on host copies of the device arrays before launching; the release build
+// trusts them (a violation races on the device).
+#ifdef PA_DEBUG
+constexpr bool kDebugChecks = true;
+#else
+constexpr bool kDebugChecks = false;
+#endif
 
 struct pa_pool {
   pa_pool_desc desc;
@@ -205,6 +215,23 @@ int prepare_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs
 extern "C" {
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t pa_debug_build(void) { return kDebugChecks ? 1 : 0; }
+
+int pa_check_slots(const int64_t* slots, int32_t n_tokens, int64_t num_slots) {
+  if (n_tokens < 0 || (n_tokens > 0 && !slots)) return fail(PA_E_INVAL, "bad arguments");
+  std::string why;
+  if (!pa::slots_are_unique(slots, n_tokens, num_slots, &why)) return fail(PA_E_INVAL, "%s", why.c_str());
+  return ok();
+}
+
+int pa_check_copy_pairs(const int32_t* pairs, int32_t n_pairs, int32_t num_blocks) {
+  if (n_pairs < 0 || (n_pairs > 0 && !pairs)) return fail(PA_E_INVAL, "bad arguments");
+  std::string why;
+  if (!pa::copy_pairs_are_disjoint(pairs, n_pairs, num_blocks, &why))
+    return fail(PA_E_INVAL, "%s", why.c_str());
+  return ok();
+}
 
 int64_t pa_block_bytes(const pa_pool_desc* desc) {
   int st = check_desc(desc);
@@ -445,6 +472,34 @@ int pa_export_free_stack(const pa_pool* pool, int32_t* out, int32_t cap, int32_t
   return ok();
 }
 
+// Debug build only: a host copy of a device array, ordered after the stream's earlier
+// work (the call then waits for the stream).
+extern "C++" {
+template <class T>
+static int fetch_to_host(const T* dev, int64_t n, hipStream_t s, std::vector<T>* host,
+                         const char* what) {
+  host->resize(static_cast<size_t>(n));
+  if (n == 0) return PA_OK;
+  hipError_t e = hipMemcpyAsync(host->data(), dev, static_cast<size_t>(n) * sizeof(T),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return hip_status(e, what);
+}
+}
+
+// Debug build: the slots of a cache write are distinct (pa_check_slots).
+static int debug_check_slots(const pa::CacheWrite& w, int32_t n_tokens, hipStream_t s,
+                             const char* what) {
+  if (!kDebugChecks || w.total_chunks == 0) return PA_OK;
+  std::vector<int64_t> h;
+  int st = fetch_to_host(w.slots, n_tokens, s, &h, what);
+  if (st) return st;
+  std::string why;
+  if (!pa::slots_are_unique(h.data(), n_tokens, w.num_slots, &why))
+    return fail(PA_E_INVAL, "%s: %s", what, why.c_str());
+  return PA_OK;
+}
+
 // Checks a cache write's arguments and fills `w`; n_tokens == 0 gives total_chunks 0.
 static int prepare_cache_write(pa_pool* pool, int32_t layer, const void* k, const void* v,
                                const int64_t* slots, int32_t n_tokens, pa::CacheWrite* w) {
@@ -484,9 +539,11 @@ static int prepare_cache_write(pa_pool* pool, int32_t layer, const void* k, cons
 int pa_reshape_and_cache(pa_pool* pool, int32_t layer, const void* k, const void* v,
                          const int64_t* slots, int32_t n_tokens, void* stream) {
   pa::CacheWrite w;
-  const int st = prepare_cache_write(pool, layer, k, v, slots, n_tokens, &w);
+  int st = prepare_cache_write(pool, layer, k, v, slots, n_tokens, &w);
   if (st) return st;
   if (w.total_chunks == 0) return ok();
+  st = debug_check_slots(w, n_tokens, static_cast<hipStream_t>(stream), "pa_reshape_and_cache");
+  if (st) return st;
   return hip_status(pa::launch_reshape_and_cache(w, static_cast<hipStream_t>(stream)),
                     "pa_reshape_and_cache");
 }
@@ -500,6 +557,15 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
   if (2 * pool->desc.num_layers > 65535) return fail(PA_E_UNSUPPORTED, "too many layers");
   const int64_t block_bytes = pool->array_bytes / pool->desc.num_blocks;
   if (block_bytes % 16 != 0) return fail(PA_E_UNSUPPORTED, "per-layer block bytes not a multiple of 16");
+  if (kDebugChecks) {
+    std::vector<int32_t> h;
+    st = fetch_to_host(pairs, 2 * static_cast<int64_t>(n_pairs), static_cast<hipStream_t>(stream), &h,
+                       "pa_copy_blocks");
+    if (st) return st;
+    std::string why;
+    if (!pa::copy_pairs_are_disjoint(h.data(), n_pairs, pool->desc.num_blocks, &why))
+      return fail(PA_E_INVAL, "pa_copy_blocks: %s", why.c_str());
+  }
   return hip_status(pa::launch_copy_blocks(pairs, n_pairs, pool->dev_base, 2 * pool->desc.num_layers,
                                            pool->desc.num_blocks, block_bytes,
                                            static_cast<hipStream_t>(stream)),
@@ -615,6 +681,8 @@ static int cache_and_decode(pa_pool* pool, int32_t layer, const void* k, const v
                       workspace_bytes, &c, window);
   if (st) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = debug_check_slots(w, n_tokens, s, what);
+  if (st) return st;
   if (c.args.num_seqs == 0) {
     if (w.total_chunks == 0) return ok();
     return hip_status(pa::launch_reshape_and_cache(w, s), what);
@@ -743,7 +811,11 @@ int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_
   a.block_size = d.block_size;
   a.block_shift = __builtin_ctz(static_cast<unsigned>(d.block_size));
   a.max_context = max_context;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  // The kernel takes a positive score scale; the caller's sign goes into the queries
+  // (a sign flip of each 16-bit element, exact) and a zero scale zeroes them.
+  a.scale_log2 = (scale == 0.0f ? 1.0f : std::fabs(scale)) * 1.4426950408889634f;
+  a.q_and = scale == 0.0f ? 0u : 0xffffffffu;
+  a.q_xor = scale < 0.0f ? 0x80008000u : 0u;
   a.part_keys = pa::kPrefillPartKeys;
   a.pmax = static_cast<int32_t>(prefill_pmax(max_context));
   a.part_o = nullptr;
