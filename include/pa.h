@@ -381,6 +381,27 @@ int pa_cache_and_decode(pa_pool* pool, int32_t layer, const void* k, const void*
                         int32_t partition_tokens, float* out, void* workspace,
                         int64_t workspace_bytes, void* stream);
 
+/* pa_cache_and_decode_static: pa_cache_and_decode for callers that cannot allocate
+ *   device memory (code under HIP graph capture, tight serving loops, harnesses that
+ *   forbid hipMalloc): the decode workspace is the library's own, a static device array
+ *   of pa_static_scratch_bytes() bytes (32 MiB) on each GPU the library runs on, held
+ *   until the process ends.  The call allocates nothing: no hipMalloc or hipFree, no
+ *   allocating library routine.  Every argument is pa_cache_and_decode's without the
+ *   workspace; the caller still owns q, the tables, the new rows and out.  A decode whose
+ *   workspace (pa_decode_workspace_bytes) exceeds the array is refused with PA_E_RANGE
+ *   before anything is launched.  Every call on a GPU shares that GPU's array, which
+ *   keeps the last call's contents (nothing needs clearing: each call's plan rewrites
+ *   the work list and the counter), so calls that overlap on one GPU (two streams, two
+ *   threads) race: serialize them.  Outputs and cache contents equal pa_cache_and_decode's
+ *   with the same arguments, bit for bit. */
+int64_t pa_static_scratch_bytes(void);
+int pa_cache_and_decode_static(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                               const int64_t* slots, int32_t n_tokens, const void* q,
+                               int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
+                               int32_t max_blocks, const int32_t* context_lens,
+                               int32_t max_context, float scale, int32_t partition_tokens,
+                               float* out, void* stream);
+
 /* Sliding-window decode: pa_decode in which sequence s attends only to its last
  *   `window` tokens, [max(0, L_s - window), L_s) ("vLLM explained", table of when KV may be
  *   overwritten: with a sliding-window model the KV outside the window can be dropped).

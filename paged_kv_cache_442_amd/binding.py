@@ -98,6 +98,9 @@ _SIGNATURES = {
     "pa_host_block_refcount": (ctypes.c_int, [_P, _I32, _PI32]),
     "pa_export_host_free_stack": (ctypes.c_int, [_P, _PI32, _I32, _PI32]),
     "pa_swap_blocks": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _I32, _P]),
+    "pa_static_scratch_bytes": (_I64, []),
+    "pa_cache_and_decode_static": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P,
+                                                  _I32, _P, _I32, ctypes.c_float, _I32, _P, _P]),
     "pa_check_slots": (ctypes.c_int, [_PI64, _I32, _I64]),
     "pa_check_copy_pairs": (ctypes.c_int, [_PI32, _I32, _I32]),
     "pa_debug_build": (_I32, []),
@@ -559,6 +562,26 @@ def pa_cache_and_decode(pool, layer, k, v, slots, q, block_tables, context_lens,
     """``pa_reshape_and_cache(k, v, slots)`` then ``pa_decode(q, ...)``, in three launches."""
     _cache_and_decode(lib().pa_cache_and_decode, pool, layer, k, v, slots, q, block_tables,
                       context_lens, max_context, scale, out, workspace, partition_tokens, stream)
+
+
+def pa_static_scratch_bytes():
+    return int(lib().pa_static_scratch_bytes())
+
+
+def pa_cache_and_decode_static(pool, layer, k, v, slots, q, block_tables, context_lens,
+                               max_context, scale, out, partition_tokens=0, stream=None):
+    """``pa_cache_and_decode`` with the library's own static workspace (no allocation)."""
+    import torch
+    dt = torch_dtype(pool.desc.kv_dtype)
+    n = slots.numel()
+    if k.shape[0] != n or v.shape != k.shape:
+        raise ValueError("k, v and slots disagree on the token count")
+    S, H_q = q.shape[0], q.shape[1]
+    _check(lib().pa_cache_and_decode_static(
+        pool.handle, layer, _dev(k, dt, "k"), _dev(v, dt, "v"), _dev(slots, torch.int64, "slots"), n,
+        _dev(q, dt, "q"), S, H_q, _dev(block_tables, torch.int32, "block_tables"),
+        block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens"), max_context,
+        float(scale), partition_tokens, _dev(out, torch.float32, "out"), _stream(stream)))
 
 
 def pa_cache_and_decode_plan(pool, layer, k, v, slots, q, block_tables, context_lens, max_context,

@@ -731,6 +731,30 @@ int pa_cache_and_decode_window(pa_pool* pool, int32_t layer, const void* k, cons
                           stream);
 }
 
+int64_t pa_static_scratch_bytes(void) { return pa::kStaticScratchBytes; }
+
+int pa_cache_and_decode_static(pa_pool* pool, int32_t layer, const void* k, const void* v,
+                               const int64_t* slots, int32_t n_tokens, const void* q,
+                               int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
+                               int32_t max_blocks, const int32_t* context_lens, int32_t max_context,
+                               float scale, int32_t partition_tokens, float* out, void* stream) {
+  int st = check_device_pool(pool, layer);
+  if (st) return st;
+  const int64_t need = pa_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_context,
+                                                 partition_tokens);
+  if (need < 0) return static_cast<int>(need);
+  if (need > pa::kStaticScratchBytes)
+    return fail(PA_E_RANGE, "pa_cache_and_decode_static: this decode needs %lld bytes of "
+                "workspace, more than the %lld the library holds (use pa_cache_and_decode)",
+                static_cast<long long>(need), static_cast<long long>(pa::kStaticScratchBytes));
+  void* ws = nullptr;
+  st = hip_status(pa::static_scratch(&ws), "pa_cache_and_decode_static (scratch address)");
+  if (st) return st;
+  return cache_and_decode(pool, layer, k, v, slots, n_tokens, q, num_seqs, num_q_heads, block_tables,
+                          max_blocks, context_lens, max_context, 0, scale, partition_tokens, out,
+                          ws, pa::kStaticScratchBytes, false, "pa_cache_and_decode_static", stream);
+}
+
 int32_t pa_prefill_part_keys(void) { return pa::kPrefillPartKeys; }
 
 static int64_t prefill_pmax(int32_t max_context) {

@@ -11,6 +11,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -1107,7 +1108,33 @@ hipError_t launch_decode_typed(const DecodeArgs& a, int group, hipStream_t s) {
   }
 }
 
+// Decode workspace for callers that cannot allocate (pa_cache_and_decode_static): the
+// library's own device memory, one copy per GPU, held until the process ends.  In host
+// code this name is not a device address; only the address hipGetSymbolAddress returns
+// for the current device is (static_scratch below).
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 }  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, int dtype, int group, hipStream_t s) {
   (void)hipGetLastError();

@@ -35,6 +35,13 @@ struct DecodeArgs {
   float v_scale;            // V scale of an FP8 cache (1 otherwise)
 };
 
+// Bytes of the decode workspace the library holds itself, per GPU, for callers that
+// cannot allocate (pa_cache_and_decode_static).
+constexpr int64_t kStaticScratchBytes = int64_t{32} << 20;
+// The current device's address of that workspace (looked up once per device).  Every call
+// on a device shares it.
+hipError_t static_scratch(void** ptr);
+
 // The plan kernel lists the work items and zeroes the work counter; the partition
 // kernel (persistent) needs a plan on the same workspace before it.
 hipError_t launch_decode_plan(const DecodeArgs& a, hipStream_t s);
