@@ -7,9 +7,14 @@ per-partition attention, then the log-sum-exp merge of partitions).
 Inputs (pool, tables, queries) are resident in HBM before timing starts.
 
 The JSON line reports:
-  value      algorithmic K+V+Q bytes per step / step time, in GB/s;
-  roofline   the partition kernel's algorithmic bytes / its mean duration
-             (HIP events on the launch stream) against 8 TB/s HBM peak;
+  value      algorithmic K+V+Q bytes per step / step time, in GB/s, where the step time
+             is the median over regions (at least five) of the timed steps, each timed by
+             events at its boundaries only (p10 / p90 over the regions beside it);
+  roofline   the partition kernel's algorithmic bytes / its mean duration (fence-free HIP
+             events on the launch stream around each launch of an instrumented pass of
+             the same steps) against 8 TB/s HBM peak;
+  read_ceilings_GBps  what a read-only probe kernel gets from HBM over a pool-sized
+             buffer: one stream, random 4 KiB tiles, random 32 KiB tiles;
   cpu_baseline  the float64 CPU oracle timed on a bounded sample of the same
              workload (a few sequences), as GB/s of algorithmic bytes.
 """
@@ -24,10 +29,6 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
-# The partition kernel is bracketed by timing events on every EVENT_STRIDE-th timed step:
-# an event record costs the stream about a microsecond, so events on every step slowed
-# the step they measure by about 1.3%.
-EVENT_STRIDE = 5
 
 WORKLOADS = {
     "llama3_70b": "Llama-3-70B-shaped GQA decode layer: 128 seqs, 64 query / 8 KV heads, d 128, "
@@ -235,33 +236,103 @@ def copy_ceiling_gbps(torch, nbytes=1 << 30, reps=20):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def read_ceiling_gbps(torch, nbytes=1 << 30, reps=20):
-    """Read-only GB/s of a plain device reduction over ``nbytes`` (a measured ceiling)."""
-    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        a.sum()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        a.sum()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    del a
-    return nbytes / (ms * 1e-3) / 1e9
+def region_bounds(n, min_regions=5, min_steps=50):
+    """Step indices cutting K = n timed steps into regions: at least ``min_regions``, each
+    of at least ``min_steps`` steps when n allows it (else min_regions equal regions)."""
+    regions = max(min_regions, n // min_steps) if n >= min_regions * min_steps else min_regions
+    regions = max(1, min(regions, n))
+    return [round(i * n / regions) for i in range(regions + 1)]
+
+
+def read_ceilings(torch, pool_bytes, reps=10, log=None):
+    """Read-only GB/s that the memory system delivers to a kernel that only reads
+    (libpa_probe.so), over a buffer the size of the decode pool, for three patterns: one
+    contiguous stream (64 KiB tiles in order), random 4 KiB tiles (the decode kernel's
+    pattern: one tile per block and KV head) and random 32 KiB tiles (all 8 KV heads of a
+    block as one run).  Two ways of reading, each swept over its depth: "wg" (a workgroup
+    reads whole tiles, 1-8 tiles in flight per workgroup, 1-8 workgroups of 256 threads
+    per CU) and "interleaved" (consecutive threads of the whole grid read consecutive
+    16-byte chunks, 4 in flight per thread, 1-16 workgroups per CU).  Each figure is the
+    mean over ``reps`` launches timed by events; the best per pattern is reported with the
+    configuration that reached it, the whole sweep goes to ``log``."""
+    import ctypes
+    from paged_kv_cache_442_amd.build import PROBE_LIB_PATH
+    if not os.path.exists(PROBE_LIB_PATH):
+        raise RuntimeError("libpa_probe.so is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    inter = lib.pa_probe_read_tiles
+    inter.restype = ctypes.c_int
+    inter.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                      ctypes.c_void_p, ctypes.c_void_p]
+    wg = lib.pa_probe_read_tiles_wg
+    wg.restype = ctypes.c_int
+    wg.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = max(1 << 30, (pool_bytes + (1 << 20) - 1) >> 20 << 20)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(16 * cus, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {}
+    rng = np.random.default_rng(0)
+
+    def timed(launch, nbytes_read):
+        if launch() != 0:
+            raise RuntimeError("read probe launch failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return nbytes_read / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+
+    for name, tile, shuffle in (("stream", 1 << 16, False), ("random_4KiB", 4096, True),
+                                ("random_32KiB", 32768, True)):
+        n_tiles = nbytes // tile
+        order = rng.permutation(n_tiles) if shuffle else np.arange(n_tiles)
+        assert order.max() < n_tiles and order.min() >= 0
+        ids = torch.from_numpy(order.astype(np.int32)).cuda()
+        args = (buf.data_ptr(), ids.data_ptr(), n_tiles, tile)
+        best, where = 0.0, None
+        for per_cu in (1, 2, 4, 8):
+            for u in (1, 2, 4, 8):
+                g = timed(lambda: wg(*args, per_cu * cus, u, sink.data_ptr(), stream.cuda_stream),
+                          n_tiles * tile)
+                kib = per_cu * cus * u * tile / 1024
+                if log:
+                    print("[read probe] %-13s wg  %d WG/CU x %d tiles in flight (%7.0f KiB chip-wide): "
+                          "%7.1f GB/s" % (name, per_cu, u, kib, g), file=log, flush=True)
+                if g > best:
+                    best, where = g, "wg: %d workgroups/CU, %d tiles in flight each" % (per_cu, u)
+        for per_cu in (1, 2, 4, 8, 16):
+            g = timed(lambda: inter(*args, per_cu * cus, sink.data_ptr(), stream.cuda_stream),
+                      n_tiles * tile)
+            if log:
+                print("[read probe] %-13s interleaved %2d WG/CU x 64 B per thread: %7.1f GB/s"
+                      % (name, per_cu, g), file=log, flush=True)
+            if g > best:
+                best, where = g, "interleaved: %d workgroups/CU, 4 loads in flight per thread" % per_cu
+        out[name] = {"GBps": round(best, 1), "config": where}
+    out["bytes_read"] = int(nbytes)
+    del buf
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=250,
+                    help="timed steps K (cut into at least 5 regions of at least 50 steps)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="llama3_70b")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline (0 disables it)")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--no-read-ceilings", action="store_true",
+                    help="skip the read-probe sweep (e.g. under a profiler)")
     ap.add_argument("--num-q-heads", type=int, default=0,
                     help="diagnostic: query heads of the llama3_70b shape (default 64)")
     ap.add_argument("--kv-fp8", action="store_true",
@@ -327,42 +398,52 @@ def main():
     torch.cuda.synchronize()
 
     n = args.steps
-    # The timed region: K steps.  The only events inside it bracket the partition kernel,
-    # whose duration the roofline needs, on every EVENT_STRIDE-th step (at least one):
-    # they skip the system-scope fence (see FenceFreeEvents), and the step time carries
-    # what they still cost.
-    sampled = list(range(0, n, EVENT_STRIDE))
-    ev = FenceFreeEvents(2 * len(sampled))
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-
-    def steps():
-        for i in range(n):
-            sess.cache_and_decode_plan()       # the cache write and the plan: one launch
-            if i % EVENT_STRIDE == 0:
-                j = i // EVENT_STRIDE
-                ev.record(2 * j, stream)
-                sess.decode_partitions()
-                ev.record(2 * j + 1, stream)
-            else:
-                sess.decode_partitions()
-            sess.decode_reduce()
-
+    # The timed region: exactly K steps of pa_cache_and_decode, synchronized on both sides,
+    # cut into regions (at least five, of at least 50 steps when K allows) by fence-free
+    # events at the region boundaries only: no event inside a region.  `value` comes from
+    # the median region's step time; p10 / p90 over the regions are reported beside it.
+    bounds = region_bounds(n)
+    rev = FenceFreeEvents(len(bounds))
     # One untimed pass over the same events first: the first records of new events cost
     # the stream several microseconds more than later ones.
-    steps()
+    for i in range(len(bounds)):
+        rev.record(i, stream)
+        sess.step()
     torch.cuda.synchronize()
-    t_start.record(stream)
-    steps()
-    t_stop.record(stream)
+    t_wall = time.perf_counter()
+    rev.record(0, stream)
+    for r in range(1, len(bounds)):
+        for _ in range(bounds[r] - bounds[r - 1]):
+            sess.step()
+        rev.record(r, stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_stop)
-    ms_step = total_ms / n
-    part_ms = np.array([ev.elapsed_ms(2 * j, 2 * j + 1) for j in range(len(sampled))])
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    region_ms = np.array([rev.elapsed_ms(r - 1, r) / (bounds[r] - bounds[r - 1])
+                          for r in range(1, len(bounds))])
+    rev.close()
+    ms_step = float(np.median(region_ms))
+    total_ms = float(np.sum(region_ms * np.diff(bounds)))
+
+    # The instrumented pass (after the timed region, same steps, same stream): fence-free
+    # events around every partition-kernel launch of K steps, for the roofline.
+    ev = FenceFreeEvents(2 * n)
+
+    def instrumented():
+        for i in range(n):
+            sess.cache_and_decode_plan()       # the cache write and the plan: one launch
+            ev.record(2 * i, stream)
+            sess.decode_partitions()
+            ev.record(2 * i + 1, stream)
+            sess.decode_reduce()
+
+    instrumented()                             # untimed: first records of the events
+    torch.cuda.synchronize()
+    instrumented()
+    torch.cuda.synchronize()
+    part_ms = np.array([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(n)])
     ev.close()
 
-    # Outside the timed region: the other kernels' times (events around every kernel) and
-    # the step time with no events inside the loop at all.
+    # Outside the timed region: the other kernels' times (events around every kernel).
     nb = min(n, 20)
     bev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nb)]
     for e in bev:
@@ -392,7 +473,6 @@ def main():
         torch.cuda.synchronize()
         return u0.elapsed_time(u1) / n
 
-    ms_step_plain = plain_ms(sess.step)
     ms_step_separate = plain_ms(sess.step_separate)
 
     part_avg_s = float(part_ms.mean()) * 1e-3
@@ -434,7 +514,7 @@ def main():
     waste = 1.0 - float(lens.sum()) / (blocks * w.block_size)
 
     ceiling = None if args.no_copy_ceiling else copy_ceiling_gbps(torch)
-    rceiling = None if args.no_copy_ceiling else read_ceiling_gbps(torch)
+    rceiling = None if args.no_read_ceilings else read_ceilings(torch, sess.storage.numel(), log=sys.stderr)
 
     line = {
         "metric": "paged-decode KV GB/s and % of HBM peak at 1 MI355X; tokens/sec per layer",
@@ -463,8 +543,12 @@ def main():
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
-        "ms_per_step_no_events": round(ms_step_plain, 5),
-        "ms_per_step_no_events_four_launches": round(ms_step_separate, 5),
+        "ms_per_step_p10_p50_p90": [round(float(x), 5) for x in np.percentile(region_ms, [10, 50, 90])],
+        "timing": {"regions": len(bounds) - 1, "steps_per_region": [int(x) for x in np.diff(bounds)],
+                   "statistic": "median of the regions' mean step times (fence-free events at "
+                                "region boundaries only)",
+                   "timed_steps_gpu_ms": round(total_ms, 4), "timed_steps_wall_ms": round(wall_ms, 3)},
+        "ms_per_step_four_launches": round(ms_step_separate, 5),
         "partition_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(part_ms, [10, 50, 90])],
         "kernel_ms": {"cache_write_and_plan": round(float(fused_ms.mean()), 5),
                       "decode_partitions": round(float(part_ms.mean()), 5),
@@ -478,7 +562,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "launches_timed": "%d of %d (one timed step in %d)" % (len(sampled), n, EVENT_STRIDE),
+            "launches_timed": "%d, by fence-free HIP events around each partition launch in an "
+                              "instrumented pass of %d steps right after the timed region" % (n, n),
             # The committed counters belong to the Llama-3-70B run at 2048-token partitions.
             "traffic": counter_traffic(os.path.dirname(os.path.abspath(__file__)))
             if (args.workload == "llama3_70b" and not args.kv_fp8 and not args.num_q_heads
@@ -486,7 +571,7 @@ def main():
                 and part_tokens == 2048) else None,
         },
         "copy_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
-        "read_ceiling_GBps": None if rceiling is None else round(rceiling, 1),
+        "read_ceilings_GBps": rceiling,
         "max_abs_err_sampled": worst,
         "internal_waste_pct": round(100 * waste, 3),
         "host_manager_us_per_step": round(host_mgr_us, 1),

@@ -1,4 +1,5 @@
-"""Build ``libpa.so`` and its debug twin ``libpa_debug.so`` in-tree with hipcc for gfx950.
+"""Build ``libpa.so``, its debug twin ``libpa_debug.so`` and the read-bandwidth probes
+``libpa_probe.so`` (bench.py's measured ceilings) in-tree with hipcc for gfx950.
 
 ``python -m paged_kv_cache_442_amd.build`` (or ``build_library()``) always recompiles.
 Each source is compiled once to an object (in parallel); the C-ABI layer is compiled
@@ -20,6 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libpa.so")
 DEBUG_LIB_PATH = os.path.join(HERE, "libpa_debug.so")
+# Read-bandwidth probes for bench.py's measured ceilings (not part of the attention path).
+PROBE_LIB_PATH = os.path.join(HERE, "libpa_probe.so")
 
 SOURCES = ["capi.cpp", "block_manager.cpp", "preconditions.cpp", "kernels.hip", "prefill.hip"]
 
@@ -66,7 +69,7 @@ def build_library(verbose=False):
     compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
     with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
         objs, cmds = {}, []
-        for src in SOURCES + ["capi.cpp#debug"]:
+        for src in SOURCES + ["capi.cpp#debug", "probes.hip"]:
             name, _, variant = src.partition("#")
             obj = os.path.join(tmp, name.replace(".", "_") + ("_debug" if variant else "") + ".o")
             extra = ["-DPA_DEBUG"] if variant else []
@@ -79,8 +82,10 @@ def build_library(verbose=False):
             members = [objs[capi]] + [objs[s] for s in SOURCES if s != "capi.cpp"]
             links.append([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + members +
                          ["-o", path + ".tmp%d" % os.getpid()])
+        links.append([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", objs["probes.hip"],
+                      "-o", PROBE_LIB_PATH + ".tmp%d" % os.getpid()])
         _run_all(links, verbose)
-        for path in (LIB_PATH, DEBUG_LIB_PATH):
+        for path in (LIB_PATH, DEBUG_LIB_PATH, PROBE_LIB_PATH):
             os.replace(path + ".tmp%d" % os.getpid(), path)
     return LIB_PATH
 
