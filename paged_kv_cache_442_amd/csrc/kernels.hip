@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -179,7 +180,10 @@ struct DecodeLds {
   // Each row of o is padded by 4 floats, and dims are stored permuted (see o_pos) so
   // that the lanes of a row write 16 consecutive 16-byte pieces: no bank conflicts.
   static constexpr int kRow = kHeadDim + 4;
-  float o[kDecodeWaves][GW][TG][kRow];
+  // Rows of partial sums per head: one per DPP row for the row-broadcast PV, one for the
+  // MFMA PV of e4m3 caches at groups of 4 or 8, which sums all of a wave's tokens.
+  static constexpr int kRows = (E::kBytes == 1 && GW >= 4) ? 1 : TG;
+  float o[kDecodeWaves][GW][kRows][kRow];
   float m[kDecodeWaves][GW];
   float l[kDecodeWaves][GW];
   // Position of dims d .. d + 3 (d a multiple of 4) within a row: the piece (d % VD) / 4
@@ -323,6 +327,27 @@ __device__ __forceinline__ f32x4 merge_partitions(const DecodeArgs& a, int64_t r
   return has_nan ? f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")} : res;
 }
 
+// PV on the matrix cores for an e4m3 cache (one step of two 16-token tiles).  w[m][d][k]
+// holds, for token pair m (token slots 2m, 2m + 1) and dword d of the lane's V chunks
+// (dims 4d .. 4d + 3 of the chunk), the bytes of dims 4d + 2k and 4d + 2k + 1 of the two
+// tokens, paired by token: [t0 dim, t1 dim, t0 dim', t1 dim'].  MFMA J takes dim J of the
+// chunk (its A row is the lane's chunk, its K index the token slot): 8 e4m3 values
+// converted exactly to bf16; the B operands are the probabilities of the same token slots,
+// as bf16 plus the bf16 rounding of the remainder.
+template <int J>
+__device__ __forceinline__ void pv_mfma_e4m3(f32x4 (&po)[8], const uint32_t (&w)[4][2][2], u32x4 bh,
+                                             u32x4 bl) {
+  if constexpr (J < 8) {
+    constexpr int d = J / 4, k = (J % 4) / 2;
+    constexpr bool hi = (J % 2) != 0;
+    const u32x4 a = {ElemFP8::to_bf16x2<hi>(w[0][d][k]), ElemFP8::to_bf16x2<hi>(w[1][d][k]),
+                     ElemFP8::to_bf16x2<hi>(w[2][d][k]), ElemFP8::to_bf16x2<hi>(w[3][d][k])};
+    po[J] = ElemBF16::mma16(a, bh, po[J]);
+    po[J] = ElemBF16::mma16(a, bl, po[J]);
+    pv_mfma_e4m3<J + 1>(po, w, bh, bl);
+  }
+}
+
 // One work unit: (sequence, KV head, partition) and the sequence's context length,
 // wave-uniform.  Everything else is derived from these four numbers when needed.
 struct Unit {
@@ -344,6 +369,9 @@ template <class E, int GW>
 constexpr int decode_blocks_per_cu() {
   // GW >= 4 with 16-bit queries runs the MFMA path; its LDS (g = 8) or, at g = 4, the
   // memory system allows two workgroups (a third or fourth measured no faster or slower).
+  // (With an e4m3 cache PV is on MFMA too; its merge needs a quarter of the LDS and its
+  // registers would allow a third workgroup, measured no faster: 0.491 / 0.499 of peak
+  // at g = 8 / 4 against 0.506 / 0.495 with two.)
   return E::kBytes == 4 ? 2 : (GW >= 4 ? 2 : 4);
 }
 
@@ -368,12 +396,30 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
   // the row that holds the V values they weight, and PV is the same row-broadcast FMA.
   constexpr bool MF = E::kQBytes == 2 && GW >= 4 && HS == 1;
   static_assert(!MF || (NCH == 16 && LOADS == 4), "MFMA scores assume 16-lane rows, 4 loads");
+  // With an e4m3 cache on the MFMA path, PV runs on MFMA too (16x16x32 over two tiles,
+  // pv_mfma_e4m3): per 32 tokens a lane's V chunks, byte-transposed in registers and
+  // converted exactly to bf16, are the A operands of 8 MFMAs (one per dim of the chunk)
+  // and its own probabilities the B operand, instead of 512 row-broadcast FMAs and the
+  // widening of every V element, which bound this path's vector unit.
+  constexpr bool PVM = MF && E::kBytes == 1;
   // Tiles per step (each wave keeps one step's K and V in flight).  The MFMA path has the
   // registers for two, but with 16-bit K/V the chip then has about 32 MiB of reads in
   // flight, more than the memory system serves best: one tile per step measured 4% faster
-  // at g = 8.  An e4m3 tile is half the bytes; at g = 4 two of them per step measured 4%
-  // faster, while at g = 8 the conversions and FMAs bound the kernel and one is faster.
-  constexpr int TS = (MF && E::kBytes == 1 && GW == 4) ? 2 : 1;
+  // at g = 8.  An e4m3 tile is half the bytes, and its PV MFMAs take two tiles.
+  constexpr int TS = PVM ? 2 : 1;
+  // Rows of partial sums per head in the LDS merge: the row-broadcast PV leaves one per
+  // DPP row (tokens of other rows), the MFMA PV sums all of a wave's tokens in one.
+  constexpr int MR = PVM ? 1 : TG;
+  static_assert(Lds::kRows == MR, "the LDS merge rows follow the PV path");
+  // K of an e4m3 cache on the MFMA path: a lane's part of its token's 128-byte row (the A
+  // operand's row is the token l % 16) is read as two 16-byte pieces, bytes 32 (l / 16)
+  // + 16 h .. + 15, so each row's line is touched by two loads instead of four 8-byte
+  // ones (the line lookups per byte were the bound: twice those of 16-bit K).  The
+  // MFMA's K index then runs over dims 32 (l / 16) + 8 s + e for slice s, and the query
+  // operand takes the same dims.
+  using KChunk = typename std::conditional<PVM, u32x4, Chunk>::type;
+  constexpr int KL = PVM ? 2 : LOADS;  // K loads per tile
+  constexpr int NKL = TS * KL;
   constexpr int NL = TS * LOADS;  // K (and V) loads per step
   constexpr int64_t kRowBytes = kHeadDim * E::kBytes;
 
@@ -466,7 +512,8 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     stage_q(qd);
   }
   bool prefetched = false;  // kr / vr already hold (or are receiving) the unit's step 0
-  Chunk kr[TS * LOADS], vr[TS * LOADS];
+  KChunk kr[NKL];
+  Chunk vr[NL];
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
 
@@ -483,7 +530,12 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
       // stay live through the tile loop and spill.
       int hs = hsel;
       asm volatile("" : "+v"(hs));
-      if constexpr (MF) {
+      if constexpr (PVM) {
+        // B operand of slice s: head hs, dims 32 rr + 8 s .. + 7 (chunk 4 rr + s).
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          qv[k] = hs < G ? s_q[hs * NCH + 4 * rr + k] : u32x4{0u, 0u, 0u, 0u};
+      } else if constexpr (MF) {
         // B operand of slice s: head hs, dims 32 s + 8 rr .. + 7 (chunk 4 s + rr).
 #pragma unroll
         for (int k = 0; k < 4; ++k)
@@ -503,11 +555,12 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     // A block id outside the pool (row offset -1) makes the unit's result NaN; such
     // tiles are read from block 0 instead, so nothing outside the pool is touched.
     const bool bad_blk = __builtin_amdgcn_ballot_w64(lane < nt && rows_cur < 0) != 0;
-    // Lane chunk offsets within the tile: K load i (MFMA: token ch, dim chunk 4 i + rr;
-    // else token 4 i + rr, chunk ch) and V load i (MFMA: token 4 rr + i, chunk ch).
-    const int k_off = MF ? ch * NCH + rr : lane;
+    // Lane chunk offsets within the tile: K load i (e4m3 on MFMA: token ch, 16-byte piece
+    // 2 rr + i; other MFMA: token ch, dim chunk 4 i + rr; else token 4 i + rr, chunk ch)
+    // and V load i (MFMA: token 4 rr + i, chunk ch).
+    const int k_off = PVM ? ch * (kHeadDim / 16) + 2 * rr : MF ? ch * NCH + rr : lane;
     const int v_off = MF ? 4 * rr * NCH + ch : lane;
-    constexpr int k_step = MF ? 4 : kWave;
+    constexpr int k_step = PVM ? 1 : MF ? 4 : kWave;
     constexpr int v_step = MF ? NCH : kWave;
     // Step n covers the wave's tiles TS n .. TS n + TS - 1.  Past the unit's steps it
     // fetches the next unit's first step (when the next unit has tiles on this wave),
@@ -526,6 +579,16 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     auto load_one = [&](const char* base, int rows, int off, int idx) -> Chunk {
       const Chunk* src = reinterpret_cast<const Chunk*>(base + static_cast<int64_t>(rows) * kRowBytes) + off;
       return __builtin_nontemporal_load(src + idx);
+    };
+    auto issue_k = [&](int n) {
+#pragma unroll
+      for (int u = 0; u < TS; ++u) {
+        const int rows = rows_of(n, u);
+        const KChunk* src =
+            reinterpret_cast<const KChunk*>(kbase + static_cast<int64_t>(rows) * kRowBytes) + k_off;
+#pragma unroll
+        for (int i = 0; i < KL; ++i) kr[u * KL + i] = __builtin_nontemporal_load(src + i * k_step);
+      }
     };
     auto issue = [&](int n, const char* base, Chunk (&r)[NL], int off, int step) {
 #pragma unroll
@@ -576,15 +639,18 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     };
 
     if (nt > 0 && !prefetched) {
-      issue(0, kbase, kr, k_off, k_step);
+      issue_k(0);
       issue(0, vbase, vr, v_off, v_step);
     }
 
-    float o[GW][VD];
+    float o[PVM ? 1 : GW][PVM ? 1 : VD];  // row-broadcast PV: o[head][element of the chunk]
+    f32x4 po[PVM ? 8 : 1];                // MFMA PV: po[J][r] = dim 32 (l / 16) + 8 r + J, head l % 16
 #pragma unroll
-    for (int h = 0; h < GW; ++h)
+    for (int h = 0; h < (PVM ? 1 : GW); ++h)
 #pragma unroll
-      for (int e = 0; e < VD; ++e) o[h][e] = 0.0f;
+      for (int e = 0; e < (PVM ? 1 : VD); ++e) o[h][e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < (PVM ? 8 : 1); ++j) po[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float m_ref = -INFINITY;  // reference maximum of head hsel (same on all its lanes)
     float l_acc = 0.0f;       // sum of this lane's probabilities (head hsel, its rows)
 
@@ -605,10 +671,19 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
         for (int u = 0; u < TS; ++u) {
           acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int k = 0; k < 4; ++k) acc[u] = E::mma16(E::k_operand(kr[u * LOADS + k]), qv[k], acc[u]);
+          for (int k = 0; k < 4; ++k) {
+            if constexpr (PVM) {
+              // Slice k: bytes 8 (k % 2) .. + 7 of piece k / 2.
+              const KChunk& piece = kr[u * KL + k / 2];
+              const u32x2 half8 = {piece[2 * (k % 2)], piece[2 * (k % 2) + 1]};
+              acc[u] = E::mma16(ElemFP8::k_operand(half8), qv[k], acc[u]);
+            } else {
+              acc[u] = E::mma16(E::k_operand(kr[u * LOADS + k]), qv[k], acc[u]);
+            }
+          }
         }
         if (n == load_step) load_next();
-        issue(n + 1, kbase, kr, k_off, k_step);
+        issue_k(n + 1);
 #pragma unroll
         for (int u = 0; u < TS; ++u)
 #pragma unroll
@@ -632,7 +707,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
           }
         }
         if (n == load_step) load_next();
-        issue(n + 1, kbase, kr, k_off, k_step);
+        issue_k(n + 1);
         if constexpr (NCH == 32) {
           // A row spans two DPP rows: add the other half of the row first.
 #pragma unroll
@@ -666,15 +741,70 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
         const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
         l_acc *= alpha;
         m_ref = m_new;
+        if constexpr (PVM) {
+          // The lane's accumulators are its own head's.
 #pragma unroll
-        for (int h = 0; h < GW; ++h) {
-          const float ah =
-              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), prob_lane<GW, MF>(h)));
+          for (int j = 0; j < 8; ++j) po[j] *= alpha;
+        } else {
 #pragma unroll
-          for (int e = 0; e < VD; ++e) o[h][e] *= ah;
+          for (int h = 0; h < GW; ++h) {
+            const float ah =
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), prob_lane<GW, MF>(h)));
+#pragma unroll
+            for (int e = 0; e < VD; ++e) o[h][e] *= ah;
+          }
         }
       }
 
+      if constexpr (PVM) {
+        // Token slot 4u + i of this lane is token 4 (l / 16) + i of tile u, the token of
+        // its score z[4u + i] and of its V chunk vr[4u + i].  Rows past the context (or
+        // before the window) may hold anything, even NaN: their chunks are zeroed by
+        // select (their probabilities are 0).
+        u32x2 vv[NL];
+#pragma unroll
+        for (int u = 0; u < TS; ++u) {
+          const bool partial_tile = tile_t0(u) + kTileTokens > t_end || tile_t0(u) < t_lo;
+#pragma unroll
+          for (int i = 0; i < LOADS; ++i) {
+            vv[u * LOADS + i] = vr[u * LOADS + i];
+            if (partial_tile) {
+              const bool keep = token(u, i) < t_end && token(u, i) >= t_lo;
+              vv[u * LOADS + i] = keep ? vv[u * LOADS + i] : u32x2{0u, 0u};
+            }
+          }
+        }
+        // The next step's V loads leave now, before this step's PV.
+#pragma unroll
+        for (int u = 0; u < TS; ++u) {
+          const int vrows = rows_of(n + 1, u);
+#pragma unroll
+          for (int i = 0; i < LOADS; ++i) vr[u * LOADS + i] = load_one(vbase, vrows, v_off, i * v_step);
+        }
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        uint32_t ph[NL / 2], pl[NL / 2];
+#pragma unroll
+        for (int m = 0; m < NL / 2; ++m) {
+          const f32x2 p = f32x2{__builtin_amdgcn_exp2f(z[2 * m] - m_ref),
+                                __builtin_amdgcn_exp2f(z[2 * m + 1] - m_ref)};
+          l_acc += p.x + p.y;
+          const bf16x2_t h = __builtin_convertvector(p, bf16x2_t);
+          const f32x2 hf = __builtin_convertvector(h, f32x2);
+          const bf16x2_t e = __builtin_convertvector(f32x2{p.x - hf.x, p.y - hf.y}, bf16x2_t);
+          ph[m] = __builtin_bit_cast(uint32_t, h);
+          pl[m] = __builtin_bit_cast(uint32_t, e);
+        }
+        uint32_t w[4][2][2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const uint32_t x0 = vv[2 * m][d], x1 = vv[2 * m + 1][d];
+            w[m][d][0] = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // [x0.b0 x1.b0 x0.b1 x1.b1]
+            w[m][d][1] = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // [x0.b2 x1.b2 x0.b3 x1.b3]
+          }
+        pv_mfma_e4m3<0>(po, w, u32x4{ph[0], ph[1], ph[2], ph[3]}, u32x4{pl[0], pl[1], pl[2], pl[3]});
+      } else {
       // Each V register is reloaded with the next step's value as soon as PV has used
       // it, so the next step's V loads leave during this step's PV rather than after it.
 #pragma unroll
@@ -715,6 +845,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      }
     };
 
     for (int n = 0; n < ns; ++n) process(n);
@@ -744,12 +875,26 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
           lds.l[wave][h] = sum;
         }
       }
+      if constexpr (PVM) {
+        const int h = lane & 15;
+        if (h < GW) {
 #pragma unroll
-      for (int h = 0; h < GW; ++h)
+          for (int r = 0; r < 4; ++r) {
+            const int d = 32 * rr + 8 * r;
+            *reinterpret_cast<f32x4*>(&lds.o[wave][h][0][Lds::o_pos(d)]) =
+                f32x4{po[0][r], po[1][r], po[2][r], po[3][r]};
+            *reinterpret_cast<f32x4*>(&lds.o[wave][h][0][Lds::o_pos(d + 4)]) =
+                f32x4{po[4][r], po[5][r], po[6][r], po[7][r]};
+          }
+        }
+      } else {
 #pragma unroll
-        for (int e4 = 0; e4 < VD; e4 += 4)
-          *reinterpret_cast<f32x4*>(&lds.o[wave][h][rr][Lds::o_pos(ch * VD + e4)]) =
-              f32x4{o[h][e4], o[h][e4 + 1], o[h][e4 + 2], o[h][e4 + 3]};
+        for (int h = 0; h < GW; ++h)
+#pragma unroll
+          for (int e4 = 0; e4 < VD; e4 += 4)
+            *reinterpret_cast<f32x4*>(&lds.o[wave][h][rr][Lds::o_pos(ch * VD + e4)]) =
+                f32x4{o[h][e4], o[h][e4 + 1], o[h][e4 + 2], o[h][e4 + 3]};
+      }
       __syncthreads();
 
       const int n_parts = (it.L - window_base(it.L, a.window) + P - 1) / P;
@@ -771,7 +916,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
           const int pos = Lds::o_pos(d4);
           f32x4 sum = *reinterpret_cast<const f32x4*>(&lds.o[w][hw][0][pos]);
 #pragma unroll
-          for (int r = 1; r < TG; ++r) sum += *reinterpret_cast<const f32x4*>(&lds.o[w][hw][r][pos]);
+          for (int r = 1; r < MR; ++r) sum += *reinterpret_cast<const f32x4*>(&lds.o[w][hw][r][pos]);
           acc += W * sum;
         }
         const f32x4 res = acc / lt * a.v_scale;

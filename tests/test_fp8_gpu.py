@@ -2,6 +2,7 @@
 oracle's quantizer, and decode within 2e-3 of the oracle's attention over the values the
 oracle's own codes stand for."""
 
+import os
 import sys
 
 import numpy as np
@@ -30,16 +31,32 @@ def oracle_codes(bits, scale):
     return fp8.quantize(x, inv)
 
 
-def oracle_outputs(sess, seqs):
+def oracle_sequence(q_bits, kt, vt, k_scale, v_scale, dtype):
+    """The oracle's decode of one sequence over the values its own e4m3 codes stand for."""
+    kc = fp8.dequantize(oracle_codes(kt, k_scale), k_scale)
+    vc = fp8.dequantize(oracle_codes(vt, v_scale), v_scale)
+    return attention.contiguous_decode(dtype, q_bits, kc, vc, attention.default_scale(q_bits.shape[-1]))
+
+
+def _oracle_sequence_job(job):
+    return oracle_sequence(*job)
+
+
+def oracle_outputs(sess, seqs, workers=0):
+    """``{s: [H_q][d]}``; with ``workers`` the sequences go to a pool of spawned CPU
+    processes (numpy only: they never touch the GPU)."""
     w = sess.w
-    out = {}
+    jobs = {}
     for s in seqs:
         kt, vt = w.seq_tokens(s)
-        kc = fp8.dequantize(oracle_codes(kt, sess.k_scale), sess.k_scale)
-        vc = fp8.dequantize(oracle_codes(vt, sess.v_scale), sess.v_scale)
-        out[s] = attention.contiguous_decode(w.dtype, w.q[s], kc, vc,
-                                             attention.default_scale(w.head_dim))
-    return out
+        jobs[s] = (w.q[s], kt, vt, sess.k_scale, sess.v_scale, w.dtype)
+    if not workers:
+        return {s: oracle_sequence(*job) for s, job in jobs.items()}
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+    order = sorted(jobs, key=lambda s: -len(jobs[s][1]))
+    with ProcessPoolExecutor(max_workers=workers, mp_context=multiprocessing.get_context("spawn")) as ex:
+        return dict(zip(order, ex.map(_oracle_sequence_job, [jobs[s] for s in order])))
 
 
 def test_fp8_cache_writes_are_bit_exact():
@@ -62,8 +79,11 @@ def test_fp8_cache_writes_are_bit_exact():
     assert np.array_equal(v_gpu.cpu().numpy(), vp)
 
 
+# Groups of 8 and 4 run QK and PV on MFMA (PV over two tiles a step), groups of 1 and 2 the
+# vector path; partitions of 64 and 128 give odd tile counts per wave (a half-masked last
+# step) and many units per workgroup.
 @pytest.mark.parametrize("H_q,H_kv,part", [(64, 8, 0), (32, 8, 128), (8, 8, 64), (16, 8, 256),
-                                           (8, 4, 512)])
+                                           (8, 4, 512), (64, 8, 64), (32, 8, 0), (16, 4, 192)])
 def test_fp8_decode_matches_the_oracle(H_q, H_kv, part):
     announce(f"fp8 decode {H_q}/{H_kv} part={part}")
     lens = [1, 15, 16, 17, 63, 64, 65, 300, 777, 2000]
@@ -78,18 +98,34 @@ def test_fp8_decode_matches_the_oracle(H_q, H_kv, part):
     assert worst <= TOL, worst
 
 
-def test_fp8_llama3_70b_shape_sampled():
-    announce("fp8 decode, Llama-3-70B-shaped layer (128 seqs, 64/8 heads)")
-    w = wl.llama3_70b()
+@pytest.mark.parametrize("H_q", [64])
+def test_fp8_llama3_70b_shape_all_outputs(H_q):
+    announce(f"fp8 decode, Llama-3-70B-shaped layer (128 seqs, {H_q}/8 heads), every output")
+    w = wl.llama3_70b(num_q_heads=H_q)
     sess = DecodeSession(w, cache_fp8=True)
     sess.step()
     torch.cuda.synchronize()
     got = sess.out.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
-    lens = np.asarray(w.context_lens)
-    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 5, 77})
-    want = oracle_outputs(sess, seqs)
-    worst = max(float(np.max(np.abs(got[s] - want[s]))) for s in seqs)
+    want = oracle_outputs(sess, range(w.num_seqs), workers=min(12, len(os.sched_getaffinity(0))))
+    worst = max(float(np.max(np.abs(got[s] - want[s]))) for s in range(w.num_seqs))
+    assert worst <= TOL, worst
+
+
+@pytest.mark.parametrize("H_q", [64, 32])
+def test_fp8_units_outnumber_the_persistent_grid(H_q):
+    """Partitions of 64 tokens: many units per workgroup on the e4m3 MFMA path (the
+    cross-unit prefetch of two-tile steps), every output checked."""
+    lens = [int(x) for x in np.random.default_rng(H_q).integers(100, 700, size=96)]
+    assert sum(-(-L // 64) for L in lens) * 8 > 1024
+    announce(f"fp8 units > grid: {H_q}/8 heads, 96 seqs, partition 64")
+    w = wl.custom_decode(600 + H_q, wl.BF16, lens, H_q, 8, block_size=16)
+    sess = DecodeSession(w, partition_tokens=64, cache_fp8=True)
+    sess.step()
+    torch.cuda.synchronize()
+    got = sess.out.cpu().numpy().astype(np.float64)
+    want = oracle_outputs(sess, range(w.num_seqs))
+    worst = max(float(np.max(np.abs(got[s] - want[s]))) for s in range(w.num_seqs))
     assert worst <= TOL, worst
 
 

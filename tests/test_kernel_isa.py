@@ -309,11 +309,12 @@ def test_mfma_read_waits_match_the_compilers_own_padding(tmp_path):
 
 
 def test_the_mfma_scan_finds_the_read_of_the_agpr_build(tmp_path):
-    """The decode kernel for groups of 8 built for three workgroups per CU (accumulators
-    in AGPRs): the scan finds its too-early v_accvgpr_read, in the g = 8 kernels only."""
+    """The decode kernel for groups of 8 built for three workgroups per CU (the 16-bit
+    ones put their QK accumulators in AGPRs): the scan finds the too-early v_accvgpr_read,
+    in g = 8 kernels only."""
     src = open(os.path.join(build.CSRC, "kernels.hip")).read()
     kept = "return E::kBytes == 4 ? 2 : (GW >= 4 ? 2 : 4);"
-    assert kept in src
+    assert src.count(kept) == 1
     variant = tmp_path / "kernels.hip"
     variant.write_text(src.replace(kept, "return E::kBytes == 4 ? 2 : (GW == 8 ? 3 : GW >= 4 ? 2 : 4);"))
     out = tmp_path / "variant.s"
