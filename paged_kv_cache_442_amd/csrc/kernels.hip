@@ -369,10 +369,10 @@ template <class E, int GW>
 constexpr int decode_blocks_per_cu() {
   // GW >= 4 with 16-bit queries runs the MFMA path; its LDS (g = 8) or, at g = 4, the
   // memory system allows two workgroups (a third or fourth measured no faster or slower).
-  // (With an e4m3 cache PV is on MFMA too; its merge needs a quarter of the LDS and its
-  // registers would allow a third workgroup, measured no faster: 0.491 / 0.499 of peak
-  // at g = 8 / 4 against 0.506 / 0.495 with two.)
-  return E::kBytes == 4 ? 2 : (GW >= 4 ? 2 : 4);
+  // With an e4m3 cache PV is on MFMA too: its merge needs a quarter of the LDS and its
+  // registers leave room for a third workgroup (0.648 / 0.658 of peak at g = 8 / 4
+  // against 0.642 / 0.653 with two, within the spread between boxes).
+  return E::kBytes == 4 ? 2 : E::kBytes == 1 && GW >= 4 ? 3 : (GW >= 4 ? 2 : 4);
 }
 
 template <class E, int GW, int HS>

@@ -313,10 +313,10 @@ def test_the_mfma_scan_finds_the_read_of_the_agpr_build(tmp_path):
     ones put their QK accumulators in AGPRs): the scan finds the too-early v_accvgpr_read,
     in g = 8 kernels only."""
     src = open(os.path.join(build.CSRC, "kernels.hip")).read()
-    kept = "return E::kBytes == 4 ? 2 : (GW >= 4 ? 2 : 4);"
+    kept = "(GW >= 4 ? 2 : 4);"
     assert src.count(kept) == 1
     variant = tmp_path / "kernels.hip"
-    variant.write_text(src.replace(kept, "return E::kBytes == 4 ? 2 : (GW == 8 ? 3 : GW >= 4 ? 2 : 4);"))
+    variant.write_text(src.replace(kept, "(GW == 8 ? 3 : GW >= 4 ? 2 : 4);"))
     out = tmp_path / "variant.s"
     flags = [f for f in build.HIP_FLAGS if f not in ("-shared", "-fPIC")]
     res = subprocess.run([build.hipcc()] + flags + ["--cuda-device-only", "-S", "-I", build.INCLUDE,
