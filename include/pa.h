@@ -461,19 +461,23 @@ int pa_seq_release_before(pa_pool* pool, int32_t seq, int32_t token, int32_t* n_
  *   out          device fp32 [num_rows][num_q_heads][head_dim]
  *   workspace    device, caller-owned, 256-byte aligned, at least
  *                pa_prefill_workspace_bytes(pool, num_rows, num_q_heads, max_context)
- *                bytes (may be NULL when that is 0, i.e. max_context <= the part size)
- * The keys of a long row range are split in parts of pa_prefill_part_keys() keys (2048;
- * each part its own workgroup, so that no workgroup outlasts the batch); such rows are
- * combined by a log-sum-exp merge kernel on the same stream, with the parts' outputs kept
- * in the workspace.
+ *                bytes: it holds the work list (a 2304-byte header and 16 bytes per
+ *                unit, at most num_rows x key parts x num_kv_heads units) and, past one
+ *                key part, the parts' outputs and log-sum-exps
+ * The work is cut into units of (sequence, KV head, 128 / group query rows, key part): the
+ * keys of a long row range are split in parts of pa_prefill_part_keys() keys (2048), so that
+ * no unit outlasts the batch.  A plan kernel lists the units longest first, in one queue per
+ * XCD (KV heads spread over the queues); the prefill kernel then runs as many workgroups as
+ * the device holds at once, each claiming units, first from its own XCD's queue; rows whose
+ * keys span several parts are combined by a log-sum-exp merge kernel.  All three launches
+ * go on the same stream.
  * A sequence with n_s > L_s, L_s > max_context or L_s > max_blocks * block_size, or whose
  * keys touch a table id outside [0, num_blocks), gets NaN rows; nothing outside the pool
  * or the row range is read or written.  Rows not owned by any sequence are untouched.
  * Supported: head_dim 128; fp16 and bf16 caches (PA_E_UNSUPPORTED for fp32);
  * num_q_heads / num_kv_heads in {1, 2, 4, 8}; block_size a power of two >= 16; at most
- * 65535 sequences per call, and at most 2^31 - 1 workgroups: ceil(max_query_len /
- * (128 / group)) row blocks x ceil(max_context / part size) key parts x num_seqs x
- * num_kv_heads (PA_E_UNSUPPORTED beyond either). */
+ * 65535 sequences per call, and at most 2^31 - 1 row blocks: ceil(max_query_len /
+ * (128 / group)) x num_seqs (PA_E_UNSUPPORTED beyond either). */
 int64_t pa_prefill_workspace_bytes(const pa_pool* pool, int32_t num_rows, int32_t num_q_heads,
                                    int32_t max_context);
 /* Keys per part of pa_prefill_chunked's split (host only, no GPU call). */

@@ -762,14 +762,26 @@ static int64_t prefill_pmax(int32_t max_context) {
                                   pa::kPrefillPartKeys);
 }
 
+// Units the prefill work list can hold: a sequence's row blocks number at most its rows,
+// so num_rows x key parts x KV heads bounds every nondecreasing query_start.
+static __int128 prefill_work_cap(const pa_pool* pool, int32_t num_rows, int32_t max_context) {
+  return static_cast<__int128>(num_rows) * prefill_pmax(max_context) * pool->desc.num_kv_heads;
+}
+
+static int64_t round256(__int128 bytes) { return static_cast<int64_t>((bytes + 255) / 256 * 256); }
+
 int64_t pa_prefill_workspace_bytes(const pa_pool* pool, int32_t num_rows, int32_t num_q_heads,
                                    int32_t max_context) {
   if (!pool) return fail(PA_E_INVAL, "pool is NULL");
   if (num_rows < 0 || num_q_heads < 0 || max_context < 0) return fail(PA_E_INVAL, "negative size");
   const int64_t pmax = prefill_pmax(max_context);
-  if (pmax == 1) return 0;
-  const __int128 items = static_cast<__int128>(num_rows) * num_q_heads * pmax;
-  const __int128 bytes = items * pa::kHeadDim * 4 + ((items * 4 + 255) / 256) * 256;
+  const __int128 cap = prefill_work_cap(pool, num_rows, max_context);
+  if (cap > 0x7fffffff) return fail(PA_E_RANGE, "more than 2^31 - 1 prefill work units");
+  __int128 bytes = pa::kPrefillHeaderBytes + round256(cap * 16);
+  if (pmax > 1) {
+    const __int128 items = static_cast<__int128>(num_rows) * num_q_heads * pmax;
+    bytes += items * pa::kHeadDim * 4 + round256(items * 4);
+  }
   if (bytes > std::numeric_limits<int64_t>::max() / 2) return fail(PA_E_RANGE, "workspace too large");
   return static_cast<int64_t>(bytes);
 }
@@ -810,15 +822,12 @@ int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_
       return fail(PA_E_INVAL, "q and out must be 16-byte aligned");
   if (num_seqs > 65535 || d.num_kv_heads > 65535)
     return fail(PA_E_UNSUPPORTED, "more than 65535 sequences or KV heads in one call");
-  {
-    const int64_t rows_per_block = pa::kPrefillColumns / group;
-    const int64_t workgroups = (max_query_len + rows_per_block - 1) / rows_per_block *
-                               prefill_pmax(max_context) * num_seqs * d.num_kv_heads;
-    if (workgroups > 0x7fffffff)
-      return fail(PA_E_UNSUPPORTED, "%lld workgroups (row blocks x key parts x sequences x KV "
-                  "heads) exceed 2^31 - 1", static_cast<long long>(workgroups));
-  }
-  pa::PrefillArgs a;
+  const int64_t rows_per_block = pa::kPrefillColumns / group;
+  const int64_t row_blocks = (max_query_len + rows_per_block - 1) / rows_per_block;
+  if (row_blocks * num_seqs > 0x7fffffff)
+    return fail(PA_E_UNSUPPORTED, "%lld row blocks (sequences x row blocks of max_query_len) "
+                "exceed 2^31 - 1", static_cast<long long>(row_blocks * num_seqs));
+  pa::PrefillArgs a{};
   a.q = q;
   a.k_cache = pool->dev_base + static_cast<int64_t>(2 * layer) * pool->array_bytes;
   a.v_cache = pool->dev_base + static_cast<int64_t>(2 * layer + 1) * pool->array_bytes;
@@ -842,9 +851,10 @@ int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_
   a.q_xor = scale < 0.0f ? 0x80008000u : 0u;
   a.part_keys = pa::kPrefillPartKeys;
   a.pmax = static_cast<int32_t>(prefill_pmax(max_context));
+  a.row_blocks = static_cast<int32_t>(row_blocks);
   a.part_o = nullptr;
   a.part_lse = nullptr;
-  if (a.pmax > 1) {
+  {
     const int64_t need = pa_prefill_workspace_bytes(pool, num_rows, num_q_heads, max_context);
     if (need < 0) return static_cast<int>(need);
     if (!workspace || workspace_bytes < need)
@@ -852,12 +862,24 @@ int pa_prefill_chunked(pa_pool* pool, int32_t layer, const void* q, int32_t num_
                   static_cast<long long>(workspace_bytes), static_cast<long long>(need));
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return fail(PA_E_INVAL, "workspace must be 256-byte aligned");
-    const int64_t items = static_cast<int64_t>(num_rows) * num_q_heads * a.pmax;
-    a.part_lse = static_cast<float*>(workspace);
-    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((items * 4 + 255) / 256) * 256);
+    // Layout: the work list's header, its units, then (with more than one key part) the
+    // parts' log-sum-exps and outputs.
+    char* base = static_cast<char*>(workspace);
+    const __int128 cap = prefill_work_cap(pool, num_rows, max_context);
+    a.work_header = reinterpret_cast<int32_t*>(base);
+    a.work_units = reinterpret_cast<int32_t*>(base + pa::kPrefillHeaderBytes);
+    a.work_cap = static_cast<int32_t>(cap);
+    base += pa::kPrefillHeaderBytes + round256(cap * 16);
+    if (a.pmax > 1) {
+      const int64_t items = static_cast<int64_t>(num_rows) * num_q_heads * a.pmax;
+      a.part_lse = reinterpret_cast<float*>(base);
+      a.part_o = reinterpret_cast<float*>(base + round256(items * 4));
+    }
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(pa::launch_prefill(a, static_cast<int>(d.kv_dtype), group, max_query_len, s),
+  st = hip_status(pa::launch_prefill_plan(a, group, s), "pa_prefill_chunked (plan)");
+  if (st) return st;
+  st = hip_status(pa::launch_prefill(a, static_cast<int>(d.kv_dtype), group, s),
                   "pa_prefill_chunked");
   if (st) return st;
   return hip_status(pa::launch_prefill_merge(a, group, max_query_len, s), "pa_prefill_chunked (merge)");

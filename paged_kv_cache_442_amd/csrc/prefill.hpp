@@ -31,6 +31,12 @@ struct PrefillArgs {
   int32_t part_keys, pmax;
   float* part_o;              // [num_rows][Hq][pmax][128]
   float* part_lse;            // [num_rows][Hq][pmax]
+  // Work list of the persistent kernel, written by the plan kernel: one queue per XCD,
+  // each a run of units (sequence, KV head, row block, key part) longest first.
+  int32_t* work_header;       // kPrefillHeaderBytes: per queue its start, length, claim counter
+  int32_t* work_units;        // [work_cap][4]
+  int32_t work_cap;           // units the list can hold
+  int32_t row_blocks;         // row blocks per sequence covered: ceil(max_query_len / rows per block)
 };
 
 // (row, query head) columns per workgroup: 128 / group consecutive rows of one sequence
@@ -38,15 +44,28 @@ struct PrefillArgs {
 constexpr int kPrefillColumns = 128;
 
 // Keys per part of the split (64 tiles): long enough to amortize a part's start and keep
-// few rows to merge, short enough that no single workgroup outlasts the batch.  Measured
-// on the mixed chunked-prefill batch (prefixes up to 4096 keys, chunks of 256-512 rows):
-// 193-196 us at 2048-key parts, 197 at 1536, 229 at 2560, 230 at 3072.
+// few rows to merge, short enough that no single unit outlasts the batch.  Measured on the
+// mixed chunked-prefill batch (prefixes up to 4096 keys, chunks of 256-512 rows), plan,
+// prefill and merge kernels together: 175 us at 2048-key parts, 181 at 1536, 178 at 3072,
+// 210 at 4096.
 constexpr int kPrefillPartKeys = 2048;
 
-// dtype: 1 fp16, 2 bf16; group = num_q_heads / num_kv_heads in {1, 2, 4, 8}.  The grid
-// covers max_query_len rows of every sequence.
-hipError_t launch_prefill(const PrefillArgs& a, int dtype, int group, int max_query_len,
-                          hipStream_t s);
+// Work queues of the persistent prefill kernel: one per XCD, so that the units of one
+// (sequence, KV head), which read the same keys, share that XCD's L2.
+constexpr int kPrefillQueues = 8;
+// The work list's header: int32 [0, 8) the queues' starts in the unit list, [8, 16) their
+// lengths, and queue x's claim counter at int32 kPrefillClaimStride * (x + 1), each counter
+// in a 256-byte line of its own.
+constexpr int kPrefillClaimStride = 64;
+constexpr int64_t kPrefillHeaderBytes = 4 * kPrefillClaimStride * (kPrefillQueues + 1);
+
+// Lists the units of the batch into work_header / work_units (one workgroup); the prefill
+// kernel launched after it on the same stream claims them.  group as below.
+hipError_t launch_prefill_plan(const PrefillArgs& a, int group, hipStream_t s);
+// dtype: 1 fp16, 2 bf16; group = num_q_heads / num_kv_heads in {1, 2, 4, 8}.  Persistent:
+// as many workgroups as the device holds at once, each claiming units until the queues
+// are empty.
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int group, hipStream_t s);
 // Combines the parts of every row block that has more than one (nothing to do when
 // pmax == 1); launched after launch_prefill on the same stream.
 hipError_t launch_prefill_merge(const PrefillArgs& a, int group, int max_query_len, hipStream_t s);

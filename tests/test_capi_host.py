@@ -241,15 +241,20 @@ def test_batch_append_is_all_or_nothing():
     assert len(slots) == 2 and pairs == []
 
 
-def test_prefill_workspace_is_needed_only_past_one_part():
-    pool = host_pool(8, 16)
+def test_prefill_workspace_holds_the_work_list_and_the_parts():
+    """The work list (a 2304-byte header: queue starts and lengths, then eight claim
+    counters 256 bytes apart; then 16 bytes per unit, at most num_rows x key parts x KV
+    heads units) always; the parts' log-sum-exps and outputs only past one part."""
+    pool = host_pool(8, 16)                            # one KV head
     P = pa.pa_prefill_part_keys()
     assert P > 0 and P % 32 == 0                       # whole 32-key tiles
-    assert pa.pa_prefill_workspace_bytes(pool, 100, 4, P) == 0
+    round256 = lambda n: -(-n // 256) * 256
+    assert pa.pa_prefill_workspace_bytes(pool, 100, 4, P) == 2304 + round256(100 * 1 * 1 * 16)
+    assert pa.pa_prefill_workspace_bytes(pool, 0, 4, P) == 2304
     rows, heads, pmax = 100, 4, 3                      # 2P + 1 keys: three parts
     items = rows * heads * pmax
-    lse = -(-items * 4 // 256) * 256
-    assert pa.pa_prefill_workspace_bytes(pool, rows, heads, 2 * P + 1) == lse + items * 128 * 4
+    assert (pa.pa_prefill_workspace_bytes(pool, rows, heads, 2 * P + 1)
+            == 2304 + round256(rows * pmax * 1 * 16) + round256(items * 4) + items * 128 * 4)
 
 
 def test_decode_default_partition():
