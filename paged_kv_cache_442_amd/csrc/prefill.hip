@@ -35,6 +35,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "prefill.hpp"
 
@@ -45,14 +46,9 @@ constexpr int kWave = 64;
 constexpr int kHead = 128;    // head_dim
 constexpr int kKeys = 32;     // keys per tile
 constexpr int kCols = kPrefillColumns;  // (row, head) columns per workgroup
-constexpr int kKRow = kHead + 8;   // K tile row stride in LDS (elements), against bank conflicts
-// Transposed V tile row stride (elements): 18 dwords.  A staging store of a wave writes
-// 16 key pairs of 8 dims rows apart for each of its four 8-dim groups, 144 dwords apart:
-// 16 banks apart, so the 64 stores fill the banks twice over (at 20 dwords they were 160
-// apart and four-way conflicted).  The PV operand reads (8 bytes, 16 rows per pass) land
-// 18 dwords apart, on distinct bank pairs.
-constexpr int kVRow = kKeys + 4;
 constexpr float kRescaleSlack = 8.0f;
+// Workgroups of the prefill kernel per CU (its register budget: 512 / 3 -> 168 VGPRs).
+constexpr int kPrefillBlocksPerCu = 3;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -61,13 +57,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-// A load the compiler makes a scalar load: the address is the same for every lane and
-// the data is not written while the kernel runs.
-template <class X>
-__device__ __forceinline__ X ld_uniform(const X* p, int64_t i) {
-  return ((const __attribute__((address_space(4))) X*)(p))[i];
-}
 
 struct MmaBF16 {
   typedef __bf16 elem;
@@ -207,24 +196,113 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const Prefil
   }
 }
 
+// LDS tiles.  A tile holds 32 keys x 128 dims of K (or V) as 32 rows of 256 bytes, filled
+// by direct-to-LDS loads: lane i of a load instruction writes the 16 bytes at 16 i of the
+// instruction's 1 KiB destination, so one instruction fills 4 rows.  Within a row the
+// sixteen 16-byte chunks are permuted, so that the MFMA operand reads spread over the
+// banks: chunk c of key k sits at position c ^ (k % 8) in a K tile (an S operand read
+// takes one chunk of each of 32 consecutive keys, and any 8 consecutive keys then use 8
+// different 16-byte bank groups) and at position c ^ 2 (k % 4) in a V tile (a transposing
+// read takes 2 chunks of each of 4 consecutive keys, which then use 8 different bank
+// groups).  The permutation costs nothing: each lane simply loads the chunk that belongs
+// at its position.
+constexpr int kRowBytes = kHead * 2;
+constexpr int kTileBytes = kKeys * kRowBytes;  // 8 KiB
+constexpr int kStages = 3;                     // tiles in LDS: the one read, two in flight
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0, expcnt 6:4, lgkmcnt 11:8): every
+// LDS access of this wave done, and all but the last n vector-memory operations.
+constexpr int wait_vm_lds(int n) { return (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14); }
+
+// LDS byte address of a __shared__ object.
+template <class X>
+__device__ __forceinline__ uint32_t lds_addr(X* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) X*)(p)));
+}
+
+// One tile's four direct-to-LDS loads of this lane: 16 bytes at k_base + k_off[j] into
+// the K tile's rows filled by instruction j (LDS k_dst[j] + 16 lane), the same for V.  A
+// load writes the LDS at M0 + its instruction offset + 16 lane, so the instructions carry
+// no offset: every address is in the operands.  Written out, not through the compiler's
+// intrinsic, so that the compiler, which tracks these loads as pending LDS writes, does
+// not wait for every load in flight (the next tiles' included) before each LDS read: the
+// kernel's own waits (tile_barrier) order these loads against the reads.  The loads write
+// no register.  Each M0 write is one wait state ahead of the load that reads it, and the
+// s_nop covers a scalar base that a VALU instruction (readlane) wrote.
+__device__ __forceinline__ void dma_tile(const void* k_base, const void* v_base, uint32_t k_off0,
+                                         uint32_t k_off1, uint32_t v_off0, uint32_t v_off1,
+                                         uint32_t k_dst0, uint32_t k_dst1, uint32_t v_dst0,
+                                         uint32_t v_dst1) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %0\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %0\n\t"
+      "s_mov_b32 m0, %8\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %1\n\t"
+      "s_mov_b32 m0, %9\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, %1"
+      :
+      : "s"(k_base), "s"(v_base), "v"(k_off0), "v"(k_off1), "v"(v_off0), "v"(v_off1),
+        "s"(k_dst0), "s"(k_dst1), "s"(v_dst0), "s"(v_dst1)
+      : "memory", "m0");
+}
+
 template <class M, int G>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256, kPrefillBlocksPerCu) void prefill_kernel(const PrefillArgs a) {
   using T = typename M::elem;
   typedef T T2 __attribute__((ext_vector_type(2)));
-  constexpr int TR = kCols / G;  // query rows per workgroup
-  constexpr int kTileK = kKeys * kKRow;
-  constexpr int kTileV = kHead * kVRow;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  constexpr int TR = kCols / G;  // query rows per unit
 
-  // Two buffers of each tile: while one is read, the next tile is stored into the other,
-  // so a tile costs one barrier.
-  __shared__ __align__(16) T s_k[2 * kTileK];   // K tile, [key][dim]
-  __shared__ __align__(16) T s_vt[2 * kTileV];  // V tile transposed, [dim][key]
+  __shared__ __align__(16) unsigned char s_k[kStages][kTileBytes];
+  __shared__ __align__(16) unsigned char s_v[kStages][kTileBytes];
   __shared__ int4 s_unit;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int half = lane / 32;  // which 8 of a 16-dim slice, which 4 keys of 8
+
+  // Per-lane LDS and global offsets, the same for every tile.
+  //  Loads: instruction j (0, 1) of wave w fills rows 4 (2 w + j) .. + 3 of a tile; lane l
+  //  of it takes key kl = 4 (2 w + j) + l / 16 at position p = l % 16.  Waves 0 and 1 load
+  //  keys 0 .. 15 of a tile, waves 2 and 3 keys 16 .. 31 (the two halves' blocks differ
+  //  when blocks hold 16 keys), so every instruction reads one block.
+  //  Byte offsets within the 16 rows of the wave's half, of instruction 0; instruction 1
+  //  reads 4 rows further on, whose K chunk is permuted by key % 8 + 4: chunk c ^ 4, i.e.
+  //  byte (k_src ^ 64) + 1024 (bit 6 of k_src holds bit 2 of c); V's permutation repeats
+  //  every 4 keys: byte v_src + 1024.
+  int k_src, v_src;
+  {
+    const int kl = 4 * (2 * wave) + lane / 16, p = lane % 16;  // kl % 8 < 4
+    k_src = kRowBytes * (kl & 15) + 16 * (p ^ (kl % 8));
+    v_src = kRowBytes * (kl & 15) + 16 * (p ^ (2 * (kl % 4)));
+  }
+  //  S operand (K rows): lane l reads key l % 32, chunk 2 sl + half, at byte
+  //  256 key + 16 ((2 sl + half) ^ (key % 8)) = 128 (sl / 4) + (k_rd ^ 32 (sl % 4)) with
+  //  k_rd = 256 key + 32 ka + 16 kb, ka = (key % 8) / 2, kb = half ^ (key % 2) (the XOR
+  //  only touches the bits that hold ka).
+  const int k_rd = kRowBytes * (lane % 32) + 32 * ((lane % 8) / 2) + 16 * (half ^ (lane % 2));
+  //  PV operand (V^T by transposing reads): for dims 32 dt .. + 31 and keys 16 q + 8 j +
+  //  4 half .. + 3, lane L = l % 16 of 16-lane group g = l / 16 supplies the address of the
+  //  4 dims 32 dt + 16 (g % 2) + 4 (L % 4) .. + 3 of key 16 q + 8 j + 4 half + L / 4; lane
+  //  i of the group then receives, for e = 0 .. 3, dim 32 dt + 16 (g % 2) + i of key
+  //  16 q + 8 j + 4 half + e, i.e. its own dim's four keys.  With x = 2 (g % 2) + (L % 4) / 2
+  //  the chunk is 4 dt + x, at position (4 dt + x) ^ 2 (L / 4) = 4 (dt ^ (L / 8)) + (x ^
+  //  (2 (L / 4) % 4)): byte 256 (16 q + 8 j) + 128 (dt / 2) + (v_rd0 ^ 64 (dt % 2))
+  //  (bit 6 of v_rd[0] holds L / 8, so v_rd[1] = v_rd[0] ^ 64).
+  int v_rd0;
+  {
+    const int L = lane % 16, g = lane / 16, x = 2 * (g % 2) + (L % 4) / 2;
+    v_rd0 = kRowBytes * (4 * half + L / 4) + 16 * (x ^ (2 * (L / 4) % 4)) + 8 * (L % 2) + 64 * (L / 8);
+  }
+
   // Persistent: claim units from this XCD's queue, then, once it is empty, from the queue
   // with the most units left.  Only thread 0 claims; the unit reaches the others through
   // the LDS.  The queues' starts and lengths are read once.
@@ -236,7 +314,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 
   while (true) {
     // Every wave has read the previous unit from s_unit (a unit that writes only NaN rows
-    // passes no other barrier); s_hdr is in place.
+    // passes no other barrier) and is done with the LDS tiles; s_hdr is in place.
     __syncthreads();
     if (tid == 0) {
       int4 u = make_int4(-1, 0, 0, 0);
@@ -279,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       }
       s_unit = u;
     }
-    // Every wave sees the new unit (and is past the previous unit's LDS reads).
+    // Every wave sees the new unit.
     __syncthreads();
     const int4 unit = s_unit;
     if (unit.x < 0) break;  // uniform: the queues are empty
@@ -303,15 +381,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     const int pos_min = L - n_rows + r0 + (TR >= 32 ? (32 * wave) % TR : 0);
     const int64_t out_row = (static_cast<int64_t>(qs) + row) * a.num_q_heads + kvh * G + hh;
 
-    if (si.bad) {
-      if (part == 0 && col_ok && si.rows_ok) {
-#pragma unroll
-        for (int d4 = 0; d4 < kHead; d4 += 8)
-          *reinterpret_cast<f32x4*>(a.out + out_row * kHead + d4 + 4 * half) =
-              f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      }
-      continue;
-    }
+    // A sequence with bad metadata runs no tile: its part-0 unit writes NaN rows (where
+    // its rows lie inside the query rows) through the common epilogue.
+    if (si.bad && (part != 0 || !si.rows_ok)) continue;
+    // Largest key any column of the unit sees, and this part's tiles of 0 .. kmax.
+    const int kmax = si.bad ? -1 : L - n_rows + min(r0 + TR, n_rows) - 1;
+    const int n_parts = si.bad ? 1 : kmax / a.part_keys + 1;
+    if (part >= n_parts) continue;  // uniform (the plan lists no such unit)
+    const int t_first = part * (a.part_keys / kKeys);
+    const int n_tiles = si.bad ? 0 : min(kmax, (part + 1) * a.part_keys - 1) / kKeys - t_first + 1;  // <= 64
+
+    // Block ids of the unit's tiles, lane i holding tile t_first + i's: keys t0 .. t0 + 15
+    // lie in the block of key t0 and keys t0 + 16 .. t0 + 31 in that of key t0 + 16 (the
+    // same block once blocks hold 32 keys or more), each clamped to kmax, so that every
+    // load stays inside blocks of the sequence.  An id outside the pool makes every output
+    // of the unit NaN (and is read as block 0).
+    const int32_t* tbl = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+    const int sh = a.block_shift;
+    const int bmask = a.block_size - 1;
+    const bool upper = wave >= 2;  // this wave loads keys 16 .. 31 of every tile
+    int id = 0;
+    if (lane < n_tiles) id = tbl[min((t_first + lane) * kKeys + (upper ? kKeys / 2 : 0), kmax) >> sh];
+    const bool out_of_pool = static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks);
+    // Known to every wave at the end of the unit (__syncthreads_or there).
+    const bool wave_bad = si.bad || __builtin_amdgcn_ballot_w64(out_of_pool) != 0;
+    if (out_of_pool) id = 0;
 
     // Q^T operands: slice s covers dims 16s .. 16s + 15; lane l holds dims 16s + 8 half ..
     // + 7 of its column.
@@ -322,92 +416,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       for (int s = 0; s < 8; ++s) qb[s] = col_ok ? (qrow[2 * s + half] & a.q_and) ^ a.q_xor : u32x4{0u, 0u, 0u, 0u};
     }
 
-    // Largest key any column of the workgroup sees, and this part's tiles of 0 .. kmax.
-    const int kmax = L - n_rows + min(r0 + TR, n_rows) - 1;
-    const int n_parts = kmax / a.part_keys + 1;
-    if (part >= n_parts) continue;  // uniform (the plan lists no such unit)
-    const int t_first = part * (a.part_keys / kKeys);
-    const int n_tiles = min(kmax, (part + 1) * a.part_keys - 1) / kKeys - t_first + 1;
-
-    // Staging: thread t moves 16-byte chunk t / 16 of keys 2 (t % 16) and 2 (t % 16) + 1
-    // (one block: block sizes are powers of two >= 16).  The 16 threads of a chunk hold 16
-    // key pairs, so their stores into the transposed V tile are 16 consecutive dwords of
-    // one row (distinct banks), and each global load still reads 64 contiguous bytes of
-    // every key it touches.  Every load below is issued whatever the key: keys past kmax
-    // read an in-bounds row and are zeroed when staged, so the loads of a tile always
-    // number the same and the waits before using them stay exact.
-    const int sk = 2 * (tid % 16);
-    const int sc = tid / 16;
-    const int32_t* tbl = a.tables + static_cast<int64_t>(seq) * a.max_blocks;
+    // The K and V rows of tile r go into stage st: four direct loads per thread, whatever
+    // the keys (rows past kmax are read from the clamped blocks, inside the sequence), so
+    // that every tile's loads number the same and the waits on them stay exact.
     const int64_t run_elems = static_cast<int64_t>(a.block_size) * kHead;
-    const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * run_elems;  // one block of the array
-    const int sh = a.block_shift;
-    const int bmask = a.block_size - 1;
-    // The block ids of a tile are the same for the whole workgroup: keys t0 .. t0 + 15 lie
-    // in the block of key t0 and keys t0 + 16 .. t0 + 31 in that of key t0 + 16 (the same
-    // block once blocks hold 32 keys or more), each clamped to kmax.  They are read with
-    // scalar loads, and a thread's element offset is one of the two scalar bases (its keys'
-    // half of the tile) plus a part that does not change from tile to tile.
-    const int64_t lane_off = sc * 8 + static_cast<int64_t>(sk & bmask) * kHead;
-    const bool upper_keys = sk >= kKeys / 2;
-    bool bad_blk = false;  // a block id outside the pool (wave-uniform)
-    struct TileBase {
-      int64_t lo, hi;  // element offsets of keys t0 .. t0 + 15 and t0 + 16 .. t0 + 31
+    const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * run_elems;
+    auto issue_tile = [&](int r, int st) {
+      const int t0 = (t_first + r) * kKeys;
+      const int blk = __builtin_amdgcn_readlane(id, r);
+      const int row0 = (t0 + (upper ? kKeys / 2 : 0)) & bmask;
+      const int64_t base = blk * blk_elems + kvh * run_elems + static_cast<int64_t>(row0) * kHead;
+      const T* kc = static_cast<const T*>(a.k_cache) + base;
+      const T* vc = static_cast<const T*>(a.v_cache) + base;
+      dma_tile(kc, vc, k_src, (k_src ^ 64) + 1024, v_src, v_src + 1024,
+               __builtin_amdgcn_readfirstlane(lds_addr(&s_k[st][1024 * (2 * wave)])),
+               __builtin_amdgcn_readfirstlane(lds_addr(&s_k[st][1024 * (2 * wave + 1)])),
+               __builtin_amdgcn_readfirstlane(lds_addr(&s_v[st][1024 * (2 * wave)])),
+               __builtin_amdgcn_readfirstlane(lds_addr(&s_v[st][1024 * (2 * wave + 1)])));
     };
-    auto tile_block = [&](int t) -> TileBase {
-      const int t0 = t * kKeys;
-      int id0 = ld_uniform(tbl, min(t0, kmax) >> sh);
-      int id1 = ld_uniform(tbl, min(t0 + kKeys / 2, kmax) >> sh);
-      // Both keys are at most kmax, so both blocks hold keys this workgroup attends to.
-      if (static_cast<unsigned>(id0) >= static_cast<unsigned>(a.num_blocks)) {
-        bad_blk = true;
-        id0 = 0;
-      }
-      if (static_cast<unsigned>(id1) >= static_cast<unsigned>(a.num_blocks)) {
-        bad_blk = true;
-        id1 = 0;
-      }
-      const int64_t in_blk = static_cast<int64_t>(kvh) * run_elems + static_cast<int64_t>(t0 & bmask) * kHead;
-      return TileBase{id0 * blk_elems + in_blk, id1 * blk_elems + in_blk};
-    };
-    // Global address (elements) of this thread's first row of tile t.  The bases are
-    // copied to values first: a lane-dependent choice between two members of one object
-    // becomes a lane-dependent address into a private array (scratch memory).
-    auto tile_rows = [&](const TileBase b) -> int64_t {
-      const int64_t lo = b.lo, hi = b.hi;
-      return (upper_keys ? hi : lo) + lane_off;
-    };
-    auto issue_k = [&](const TileBase b, u32x4 (&kr)[2]) {
-      const int64_t off = tile_rows(b);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        kr[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.k_cache) + off + j * kHead);
-    };
-    auto issue_v = [&](int t, const TileBase b, u32x4 (&vr)[2], int& valid) {
-      const int key = t * kKeys + sk;
-      valid = (key <= kmax ? 1 : 0) | (key + 1 <= kmax ? 2 : 0);
-      const int64_t off = tile_rows(b);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        vr[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.v_cache) + off + j * kHead);
-    };
-    auto store_k = [&](int buf, const u32x4 (&kr)[2]) {
-      T* sk_buf = s_k + buf * kTileK;
-      *reinterpret_cast<u32x4*>(&sk_buf[sk * kKRow + sc * 8]) = kr[0];
-      *reinterpret_cast<u32x4*>(&sk_buf[(sk + 1) * kKRow + sc * 8]) = kr[1];
-    };
-    auto store_v = [&](int buf, const u32x4 (&vr)[2], int valid) {
-      T* sv_buf = s_vt + buf * kTileV;
-      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-      const u32x4 v0 = (valid & 1) ? vr[0] : z, v1 = (valid & 2) ? vr[1] : z;
-      // V transposed: dims sc * 8 .. + 7, keys sk and sk + 1 side by side.
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // Byte permutes: low halves of the two keys' dwords, then high halves.
-        const int d = sc * 8 + 2 * w;
-        *reinterpret_cast<uint32_t*>(&sv_buf[d * kVRow + sk]) = __builtin_amdgcn_perm(v1[w], v0[w], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(&sv_buf[(d + 1) * kVRow + sk]) = __builtin_amdgcn_perm(v1[w], v0[w], 0x07060302u);
-      }
+    // Wait for this thread's loads of the tile about to be read (all but the `newer` tiles'
+    // loads issued after it) and its LDS accesses, then for every wave.
+    auto tile_barrier = [&](bool newer) {
+      asm volatile("" ::: "memory");
+      if (newer)
+        __builtin_amdgcn_s_waitcnt(wait_vm_lds(4));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_vm_lds(0));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     };
 
     f32x16 o[4];
@@ -416,38 +452,49 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     float m_ref = -INFINITY;  // reference maximum of this lane's column (base 2)
     float l_part = 0.0f;      // sum of this lane's probabilities (its 16 keys of each tile)
 
-    // S^T of a tile (32 keys x this wave's 32 columns) from the K buffer kb.
-    auto scores = [&](const T* kb) -> f32x16 {
+    // One tile: scores, softmax and PV from stage ST.
+    auto step = [&](int r, auto stage) {
+      constexpr int ST = decltype(stage)::value;
+      const unsigned char* kb = s_k[ST];
+      const unsigned char* vb = s_v[ST];
+      const int t0 = (t_first + r) * kKeys;
+      // V rows past kmax (only in a unit's last tile) are zeroed: a zero probability times
+      // a NaN from unused cache memory would still be NaN.  Each thread clears the rows it
+      // loaded, after its loads landed, before every wave reads them.
+      if (t0 + kKeys - 1 > kmax) {
+        // The zeros are made here (not kept in registers through the loop).
+        u32x4 z;
+        asm volatile("v_mov_b32 %0, 0\n\tv_mov_b32 %1, 0\n\tv_mov_b32 %2, 0\n\tv_mov_b32 %3, 0"
+                     : "=v"(z.x), "=v"(z.y), "=v"(z.z), "=v"(z.w));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int kl = 4 * (2 * wave + j) + lane / 16;
+          if (t0 + kl > kmax) *reinterpret_cast<u32x4*>(&s_v[ST][1024 * (2 * wave + j) + 16 * lane]) = z;
+        }
+        tile_barrier(false);
+      }
+      // S^T (32 keys x this wave's 32 columns).
       f32x16 s = f32x16{};
 #pragma unroll
       for (int sl = 0; sl < 8; ++sl) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(&kb[(lane % 32) * kKRow + 16 * sl + 8 * half]);
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(kb + (k_rd ^ (32 * (sl % 4))) + 128 * (sl / 4));
         s = M::mma(ka, qb[sl], s);
       }
-      return s;
-    };
-
-    // Softmax and PV of tile t, whose scores are in s, with V from the buffer vb.  The next
-    // tile's scores are computed meanwhile from the K buffer kb_next and left in s: their
-    // MFMAs do not depend on this tile's vector work, so the two interleave in the wave's
-    // instruction stream and the matrix cores run while the softmax does.
-    auto step = [&](int t, f32x16& s, const T* kb_next, const T* vb) {
-      const int t0 = t * kKeys;
       // Causal mask, only on tiles that reach past the wave's first position; lane holds
       // keys t0 + 8j + 4 half + i, j, i = 0..3.  (Columns past the chunk have pos >= L and
       // zero queries: they compute finite values that are never stored.)
       if (t0 + kKeys - 1 > pos_min) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t0 + 8 * (r / 4) + 4 * half + (r % 4);
-          s[r] = key <= pos ? s[r] : -INFINITY;
+        for (int rr = 0; rr < 16; ++rr) {
+          const int key = t0 + 8 * (rr / 4) + 4 * half + (rr % 4);
+          s[rr] = key <= pos ? s[rr] : -INFINITY;
         }
       }
       // Maximum of the raw scores (the score scale is positive: the sign of the caller's
       // scale went into the queries), then base 2.
       float tmax = s[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+      for (int rr = 1; rr < 16; ++rr) tmax = fmaxf(tmax, s[rr]);
       {
         // The column's other 16 keys sit in lane l ^ 32: swapping the wave's two halves in
         // registers (no LDS round trip) gives each lane its own value and its partner's.
@@ -467,113 +514,72 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
       }
-      const f32x16 s_next = scores(kb_next);
       // Probabilities exp2(s c - m), split into a 16-bit value and the 16-bit rounding of
       // the rest.  A column that has seen no key yet (possible in a later part of a split
       // range) keeps m = -inf: its masked scores must give 0, not -inf - -inf.
       const float mr = m_ref == -INFINITY ? 0.0f : m_ref;
       uint32_t ph[8], pl[8];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const f32x2 p = f32x2{__builtin_amdgcn_exp2f(fmaf(s[r], c, -mr)),
-                              __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -mr))};
+      for (int rr = 0; rr < 16; rr += 2) {
+        const f32x2 p = f32x2{__builtin_amdgcn_exp2f(fmaf(s[rr], c, -mr)),
+                              __builtin_amdgcn_exp2f(fmaf(s[rr + 1], c, -mr))};
         l_part += p.x + p.y;
         // Two probabilities per conversion (round to nearest even), then the remainders.
         const T2 h = __builtin_convertvector(p, T2);
         const f32x2 hf = __builtin_convertvector(h, f32x2);
         const T2 e = __builtin_convertvector(f32x2{p.x - hf.x, p.y - hf.y}, T2);
-        ph[r / 2] = __builtin_bit_cast(uint32_t, h);
-        pl[r / 2] = __builtin_bit_cast(uint32_t, e);
+        ph[rr / 2] = __builtin_bit_cast(uint32_t, h);
+        pl[rr / 2] = __builtin_bit_cast(uint32_t, e);
       }
       // O^T += V^T P^T: MFMA q covers keys 16q .. 16q + 15; its B operand is this lane's
       // probabilities 8q .. 8q + 7, whose keys (in operand order) are 16q + 4 half + i and
-      // 16q + 8 + 4 half + i, i = 0..3.
+      // 16q + 8 + 4 half + i, i = 0..3; the A operand (V^T) takes the same keys, in the same
+      // order, from two transposing reads.
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const u32x4 bh = u32x4{ph[4 * q], ph[4 * q + 1], ph[4 * q + 2], ph[4 * q + 3]};
         const u32x4 bl = u32x4{pl[4 * q], pl[4 * q + 1], pl[4 * q + 2], pl[4 * q + 3]};
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const T* vrow = &vb[(32 * dt + lane % 32) * kVRow + 16 * q + 4 * half];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-          const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
+          const unsigned char* vr = vb + (v_rd0 ^ (64 * (dt % 2))) + 128 * (dt / 2) + kRowBytes * 16 * q;
+          typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr + kRowBytes * 8));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 va = u32x4{lo2.x, lo2.y, hi2.x, hi2.y};
           o[dt] = M::mma(va, bh, o[dt]);
           o[dt] = M::mma(va, bl, o[dt]);
         }
       }
-      s = s_next;
     };
 
-    // Pipeline.  K runs one tile ahead of V: during step r (tile r of the part) the LDS
-    // holds K of tile r + 1 (buffer (r + 1) % 2, for the next scores) and V of tile r
-    // (buffer r % 2); the stores at the end of the step put K of tile r + 2 into buffer r % 2
-    // and V of tile r + 1 into buffer (r + 1) % 2, both last read in the step before.  The
-    // loads of a step's stores were issued at the top of the step before, into the other of
-    // two register sets, and block ids run one tile ahead of the K loads.  Every load is
-    // issued whatever the key: keys past kmax read an in-bounds row (K rows past it are
-    // masked through their scores, V rows zeroed when staged), so the loads in flight always
-    // number the same and the waits before the stores stay exact.
-    const T* kbuf0 = s_k;
-    const T* kbuf1 = s_k + kTileK;
-    const T* vbuf0 = s_vt;
-    const T* vbuf1 = s_vt + kTileV;
-    u32x4 kA[2], vA[2], kB[2], vB[2];
-    int mA, mB;
-    const TileBase id0 = tile_block(t_first);
-    const TileBase id1 = tile_block(t_first + 1);
-    issue_k(id0, kA);
-    issue_v(t_first, id0, vA, mA);
-    issue_k(id1, kB);
-    store_k(0, kA);
-    store_v(0, vA, mA);
-    store_k(1, kB);
-    __syncthreads();
-    f32x16 s = scores(kbuf0);
-    // Every wave has read K buffer 0 before the first step's stores overwrite it.
-    __syncthreads();
-    // The loads of the first step's stores, and the block ids of the two tiles after them.
-    TileBase id_v = tile_block(t_first + 2);  // blocks of the next V issue (tile r + 2)
-    TileBase id_k = tile_block(t_first + 3);  // blocks of the next K issue (tile r + 3)
-    issue_k(id_v, kA);
-    issue_v(t_first + 1, id1, vA, mA);
-    TileBase id_n = tile_block(t_first + 4);  // blocks of the K issue after next (tile r + 4)
-    // Pairs of steps per trip with one exit test, so that the loop header is reached only
-    // from the prologue and from the end of a pair; the scheduling barriers keep the loads
-    // ahead of the step and the stores after it.  The block ids (scalar loads) are read
-    // after a step's stores: scalar and LDS results share one wait counter, so a scalar
-    // load in flight during the step would hold up its first LDS wait, while the stores'
-    // wait before the barrier is there anyway.
-    int r = 0;
-    for (; r + 1 < n_tiles; r += 2) {
-      issue_k(id_k, kB);
-      issue_v(t_first + r + 2, id_v, vB, mB);
-      id_v = id_k;
-      id_k = id_n;
-      __builtin_amdgcn_sched_barrier(0);
-      step(t_first + r, s, kbuf1, vbuf0);
-      __builtin_amdgcn_sched_barrier(0);
-      store_k(0, kA);
-      store_v(1, vA, mA);
-      id_n = tile_block(t_first + r + 5);
-      __syncthreads();
-      issue_k(id_k, kA);
-      issue_v(t_first + r + 3, id_v, vA, mA);
-      id_v = id_k;
-      id_k = id_n;
-      __builtin_amdgcn_sched_barrier(0);
-      step(t_first + r + 1, s, kbuf0, vbuf1);
-      __builtin_amdgcn_sched_barrier(0);
-      store_k(1, kB);
-      store_v(0, vB, mB);
-      id_n = tile_block(t_first + r + 6);
-      __syncthreads();
+    // Pipeline: at step r the LDS holds tile r (stage r % 3, read now) and tiles r + 1 and
+    // r + 2 are in flight or landed (stages (r + 1) % 3, (r + 2) % 3).  Step r begins by
+    // waiting for tile r's loads (all but tile r + 1's four loads, issued after them) and a
+    // barrier, which also ends every wave's reads of stage (r + 2) % 3 = (r - 1) % 3 in
+    // step r - 1; it then issues tile r + 2's loads into that stage.
+    if (n_tiles > 0) issue_tile(0, 0);
+    asm volatile("" ::: "memory");  // tile 0's loads strictly before tile 1's
+    if (n_tiles > 1) issue_tile(1, 1);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    for (int r = 0; r < n_tiles; r += kStages) {
+      tile_barrier(r + 1 < n_tiles);
+      if (r + 2 < n_tiles) issue_tile(r + 2, 2);
+      step(r, S0{});
+      if (r + 1 >= n_tiles) break;
+      tile_barrier(r + 2 < n_tiles);
+      if (r + 3 < n_tiles) issue_tile(r + 3, 0);
+      step(r + 1, S1{});
+      if (r + 2 >= n_tiles) break;
+      tile_barrier(r + 3 < n_tiles);
+      if (r + 4 < n_tiles) issue_tile(r + 4, 1);
+      step(r + 2, S2{});
     }
-    // An odd tile count: the last step (its next scores, of a tile past the part, go unused).
-    if (r < n_tiles) step(t_first + r, s, kbuf1, vbuf0);
 
-    // A block id outside the pool anywhere in the workgroup's keys makes every output NaN.
-    bad_blk = __syncthreads_or(bad_blk);
+    // A block id outside the pool anywhere in the unit's keys makes every output NaN.
+    const bool bad_blk = __syncthreads_or(wave_bad);
     // Columns past the chunk (their partner lane l ^ 32 is the same column) write nothing.
     if (col_ok) {
       const float l_col = l_part + __shfl_xor(l_part, 32);
