@@ -634,18 +634,39 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
     if (row >= n_rows) return;
     const int64_t out_row = (static_cast<int64_t>(qs) + row) * a.num_q_heads + kvh * G + col / TR;
     const float* lse = a.part_lse + out_row * a.pmax;
+    const float* po = a.part_o + out_row * a.pmax * kHead + d4;
+    // Parts four at a time, every load of a group issued before its arithmetic (parts past
+    // n_parts read as lse -inf, weight 0).  Part 0 holds key 0, which every row sees, so M
+    // is finite unless a part is NaN.
     float M = -INFINITY;
     bool has_nan = false;
-    for (int p = 0; p < n_parts; ++p) {
-      has_nan |= lse[p] != lse[p];
-      M = fmaxf(M, lse[p]);
+    for (int p0 = 0; p0 < n_parts; p0 += 4) {
+      float l[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l[i] = p0 + i < n_parts ? lse[p0 + i] : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        has_nan |= l[i] != l[i];
+        M = fmaxf(M, l[i]);
+      }
     }
     f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float wsum = 0.0f;
-    for (int p = 0; p < n_parts; ++p) {
-      const float w = __builtin_amdgcn_exp2f(lse[p] - M);
-      wsum += w;
-      acc += w * *reinterpret_cast<const f32x4*>(a.part_o + (out_row * a.pmax + p) * kHead + d4);
+    for (int p0 = 0; p0 < n_parts; p0 += 4) {
+      float l[4];
+      f32x4 o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = p0 + i < n_parts;
+        l[i] = ok ? lse[p0 + i] : -INFINITY;
+        o[i] = ok ? *reinterpret_cast<const f32x4*>(po + (p0 + i) * kHead) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float w = __builtin_amdgcn_exp2f(l[i] - M);
+        wsum += w;
+        acc += w * o[i];
+      }
     }
     const float nan = __builtin_nanf("");
     *reinterpret_cast<f32x4*>(a.out + out_row * kHead + d4) =
