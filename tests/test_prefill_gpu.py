@@ -75,6 +75,22 @@ def test_prefill_small_shapes_all_rows(dtype, H_q, H_kv, bs):
     check_chunks(sess, lambda i: range(int(w.chunk_lens[i])))
 
 
+# The plan puts unit (sequence s, KV head h) in work queue (s * H_kv + h) mod 8, one queue per
+# XCD: with fewer than 8 KV heads the queues differ in length, and the workgroups of the
+# short queues take units from the long ones once theirs are empty.
+@pytest.mark.parametrize("dtype,H_q,H_kv,bs", [(wl.BF16, 8, 1, 16), (wl.BF16, 4, 2, 32),
+                                               (wl.F16, 2, 2, 16)])
+def test_prefill_fewer_kv_heads_than_queues_all_rows(dtype, H_q, H_kv, bs):
+    announce(f"prefill, {H_kv} KV heads over 8 work queues: dtype={dtype} H_q={H_q} bs={bs}")
+    P = pa.pa_prefill_part_keys()
+    w = wl.custom_chunked(400 + H_q + H_kv, dtype, PREFIXES + [P + 70, 3], CHUNKS + [200, 500], [],
+                          H_q, H_kv, block_size=bs)
+    sess = PrefillSession(w)
+    sess.step()
+    torch.cuda.synchronize()
+    check_chunks(sess, lambda i: range(int(w.chunk_lens[i])))
+
+
 @pytest.mark.parametrize("dtype,H_q,H_kv", [(wl.BF16, 32, 8), (wl.F16, 64, 8), (wl.BF16, 8, 8)])
 def test_prefill_split_into_parts_all_rows(dtype, H_q, H_kv):
     """Contexts past the part size are split into parts and merged; a chunk across the
