@@ -26,12 +26,15 @@
 //   * Online softmax per column (the two lanes l, l ^ 32 of a column share its maximum),
 //     base 2, with the accumulators rescaled only when a score passes the reference
 //     maximum by kRescaleSlack.
-//   * O^T += V^T P^T with the same MFMA, V staged transposed in LDS.  P goes in as two
-//     MFMA operands, its bf16 (or fp16) rounding and the rounding of the remainder, so
-//     the only error left is the fp32 accumulation (a single rounding of P could move an
-//     output by several 1e-3 on rows that see only a few keys).
-//   * Causal and length masks by select; V rows past the context are zeroed when staged
-//     (a zero probability times a NaN from unused cache memory would still be NaN).
+//   * O^T += V^T P^T with the same MFMA, V^T read from the (untransposed) V tile by
+//     transposing LDS reads.  P goes in as two MFMA operands, its bf16 (or fp16) rounding
+//     and the rounding of the remainder, so the only error left is the fp32 accumulation
+//     (a single rounding of P could move an output by several 1e-3 on rows that see only
+//     a few keys).
+//   * K and V tiles go from the cache straight into LDS (direct-to-LDS loads, three tiles
+//     in LDS: the one being read and two in flight), one barrier per tile.
+//   * Causal and length masks by select; V rows past the context are zeroed in LDS (a
+//     zero probability times a NaN from unused cache memory would still be NaN).
 #include <math.h>
 
 #include <algorithm>
