@@ -603,8 +603,13 @@ __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>(
     // number at its load step; every wave loads the next unit (descriptor, row offsets,
     // query rows) at its own load step, waiting for the publication if it gets there
     // first.  Both steps sit a few steps before the end, so that the next unit's first
-    // step can be issued by this unit's last one; short units do both at step 0.
-    constexpr int kClaimLead = 6 / TS, kLoadLead = 4 / TS;
+    // step can be issued by this unit's last one; short units do both at step 0.  With
+    // 16-bit K/V at groups of 8 (the longest units) two more steps of lead let the next
+    // unit's loads land before the switch (+0.3% at the Llama-3-70B layer, +0.8% with a
+    // 1024-token window); the same lead costs 0.5% at groups of 4 and 2% on the vector
+    // path, whose units are shorter.
+    constexpr bool kLongLead = MF && GW == 8 && !PVM;
+    constexpr int kClaimLead = (kLongLead ? 8 : 6) / TS, kLoadLead = (kLongLead ? 6 : 4) / TS;
     const int ns0 = (wave_tiles_of_stream(it, 0) + TS - 1) / TS;  // wave 0's steps
     const int claim_step = max(0, ns0 - kClaimLead);
     const int load_step = max(0, ns - kLoadLead);
