@@ -295,7 +295,7 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
  *   "vLLM explained", two implementation layers: same result as ordinary attention).
  *
  * The work is split over partitions of `partition_tokens` consecutive tokens (0 =
- * default: pa_decode_default_partition; else a positive multiple of 64, at most 2048),
+ * default: pa_decode_default_partition; else a positive multiple of 64, at most 4096),
  * run as three kernels
  * on `stream`:
  *   pa_decode_plan        lists the (sequence, partition) work items in the workspace
@@ -329,9 +329,10 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n_pairs, void* s
 int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context, int32_t partition_tokens);
 /* The partition size a decode call with partition_tokens = 0 uses for this pool and
- * num_q_heads (host only, no GPU call): 2048 tokens for fp16, bf16 and e4m3 caches at
- * groups (num_q_heads / num_kv_heads) of 4 or 8; otherwise 1024 / element bytes tokens
- * (512 for fp16/bf16, 1024 for e4m3, 256 for fp32).  Returns PA_E_INVAL (negative) for a
+ * num_q_heads (host only, no GPU call): 4096 tokens for fp16 and bf16 caches at groups
+ * (num_q_heads / num_kv_heads) of 8, 2048 for fp16 and bf16 at groups of 4 and for e4m3
+ * caches at groups of 4 or 8; otherwise 1024 / element bytes tokens (512 for fp16/bf16,
+ * 1024 for e4m3, 256 for fp32).  Returns PA_E_INVAL (negative) for a
  * NULL pool or num_q_heads that is not a positive multiple of num_kv_heads. */
 int32_t pa_decode_default_partition(const pa_pool* pool, int32_t num_q_heads);
 int pa_decode_plan(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,

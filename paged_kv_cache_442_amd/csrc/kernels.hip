@@ -379,6 +379,7 @@ template <class E, int GW, int HS>
 __global__ __launch_bounds__(kWave * kDecodeWaves, (decode_blocks_per_cu<E, GW>())) void decode_partition_kernel(const DecodeArgs a) {
   constexpr int G = GW * HS;            // query heads per KV head
   constexpr int NS = kDecodeWaves / HS;  // tile streams per workgroup
+  static_assert(NS * kWave * kTileTokens >= kMaxPartition, "a wave's tiles of a unit fit its lanes");
   using GL = GroupLayout<GW>;
   using Lds = DecodeLds<E, GW>;
   constexpr int NCH = Lds::NCH;
@@ -974,11 +975,14 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* s_tmp, int* tota
 // The plan's body: one workgroup of kPlanThreads threads runs it, alone in
 // decode_plan_kernel or beside the cache writes in cache_write_plan_kernel.
 __device__ __forceinline__ void plan_work(const DecodeArgs& a) {
-  // Partial items are listed largest first (bucketed by their number of tiles), so that
-  // the smallest units are the last ones claimed and the persistent workgroups finish
-  // together.  The order of items within a bucket is whatever the LDS counters give:
-  // a unit's result does not depend on which workgroup runs it or when.
-  constexpr int kBuckets = kMaxPartition / kTileTokens + 1;  // 0: empty or invalid
+  // Partial items are listed largest first (bucketed by their length in steps of
+  // kBucketTokens: 32 tokens, two tiles, so that the serial pass over the buckets below
+  // stays at 129), so that the smallest units are the last ones claimed and the
+  // persistent workgroups finish together.  The order of items within a bucket is
+  // whatever the LDS counters give: a unit's result does not depend on which workgroup
+  // runs it or when.
+  constexpr int kBucketTokens = kMaxPartition / 128;
+  constexpr int kBuckets = kMaxPartition / kBucketTokens + 1;  // 0: empty or invalid
   __shared__ int s_tmp[kPlanThreads / 64];
   __shared__ int s_count[kBuckets];
   __shared__ int s_next[kBuckets];
@@ -994,7 +998,7 @@ __device__ __forceinline__ void plan_work(const DecodeArgs& a) {
       const int span = L - window_base(L, a.window);  // tokens from the first partition on
       const int rem = span % P;
       *full = span / P;
-      *bucket = rem == 0 ? -1 : (rem + kTileTokens - 1) / kTileTokens;  // -1: no partial item
+      *bucket = rem == 0 ? -1 : (rem + kBucketTokens - 1) / kBucketTokens;  // -1: no partial item
     }
   };
   for (int b = threadIdx.x; b < kBuckets; b += blockDim.x) s_count[b] = 0;

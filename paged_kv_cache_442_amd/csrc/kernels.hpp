@@ -13,9 +13,9 @@ constexpr int kHeadDim = 128;        // head_dim the attention kernels are built
 constexpr int kTileTokens = 16;      // tokens per K/V tile streamed by the decode kernel
 constexpr int kDecodeWaves = 4;      // waves per decode workgroup
 constexpr int kPlanThreads = 1024;
-// A wave's tiles of one unit must fit one wave of lanes; a workgroup has at least two
-// tile streams (four waves, at most two head halves).
-constexpr int kMaxPartition = 2 * 64 * kTileTokens;
+// A wave's tiles of one unit must fit one wave of lanes; a workgroup has four tile
+// streams (four waves, each carrying its KV head's whole group of query heads).
+constexpr int kMaxPartition = 4 * 64 * kTileTokens;
 
 struct DecodeArgs {
   const void* q;            // [S][Hq][128]

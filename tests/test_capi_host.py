@@ -258,9 +258,10 @@ def test_prefill_workspace_holds_the_work_list_and_the_parts():
 
 
 def test_decode_default_partition():
-    # 2048 tokens for 16-bit and e4m3 caches at groups of 4 and 8, else 1024 / element bytes.
-    want = {pa.F32: [256, 256, 256, 256], pa.F16: [512, 512, 2048, 2048],
-            pa.BF16: [512, 512, 2048, 2048], pa.FP8_E4M3: [1024, 1024, 2048, 2048]}
+    # 4096 tokens for 16-bit caches at groups of 8; 2048 for 16-bit at groups of 4 and e4m3
+    # at groups of 4 and 8; else 1024 / element bytes.
+    want = {pa.F32: [256, 256, 256, 256], pa.F16: [512, 512, 2048, 4096],
+            pa.BF16: [512, 512, 2048, 4096], pa.FP8_E4M3: [1024, 1024, 2048, 2048]}
     for dt, parts in want.items():
         pool = pa.pa_alloc_pool(pa.make_desc(1, 4, 16, 8, 128, dt), None, None)
         try:

@@ -312,12 +312,14 @@ def test_shared_prefix_copy_on_write_end_to_end():
     assert worst <= 2e-3, worst
 
 
-@pytest.mark.parametrize("part", [0, 64, 2048])
-def test_very_long_contexts(part):
-    """Maximum-size work: 64k-token contexts next to a one-token one, at the smallest,
-    default and largest partition sizes (up to 1,094 partitions of one sequence)."""
-    announce(f"long contexts 65536 / 70001 / 1, 64/8 heads bf16, partition {part}")
-    w = wl.custom_decode(77, wl.BF16, [65536, 70001, 1], 64, 8, block_size=16)
+@pytest.mark.parametrize("H_q,part", [(64, 0), (64, 64), (64, 2048), (8, 4096)])
+def test_very_long_contexts(H_q, part):
+    """Maximum-size work: 64k-token contexts next to a one-token one, at the smallest
+    partition size, at 2048 tokens and at the default, which is the largest (4096 tokens at
+    groups of 8 with a bf16 cache): up to 1,094 partitions of one sequence; and the largest
+    on the vector path (groups of 1), 64 tiles for each of a workgroup's waves."""
+    announce(f"long contexts 65536 / 70001 / 1, {H_q}/8 heads bf16, partition {part}")
+    w = wl.custom_decode(77, wl.BF16, [65536, 70001, 1], H_q, 8, block_size=16)
     sess = DecodeSession(w, partition_tokens=part)
     sess.step()
     torch.cuda.synchronize()
