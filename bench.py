@@ -64,13 +64,13 @@ def algorithmic_bytes(w, window=0, kv_bytes=None):
     return kv + q
 
 
-def counter_traffic(root):
+def counter_traffic(root, partition_tokens):
     """HBM bytes per launch of the partition kernel from the committed rocprofv3 counters.
 
     The counters (FETCH_SIZE, WRITE_SIZE in KiB per dispatch, each scaled by what the
-    same counter reads for a plain copy of known size) hold only for the kernel source
-    they were taken on: if its fingerprint differs, the figure is stale and None is
-    returned.
+    same counter reads for a plain copy of known size) hold only for the kernel source and
+    the partition size they were taken on: if either differs, the figure is stale and None
+    is returned.
     """
     import hashlib
     path = os.path.join(root, "profiles", "decode_partition_kernel_llama3_70b.json")
@@ -78,6 +78,8 @@ def counter_traffic(root):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if rec.get("partition_tokens") != partition_tokens:
+        return None
     h = hashlib.sha256()
     for name in rec["source_files"]:
         with open(os.path.join(root, name), "rb") as f:
@@ -564,11 +566,10 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "launches_timed": "%d, by fence-free HIP events around each partition launch in an "
                               "instrumented pass of %d steps right after the timed region" % (n, n),
-            # The committed counters belong to the Llama-3-70B run at 2048-token partitions.
-            "traffic": counter_traffic(os.path.dirname(os.path.abspath(__file__)))
+            # The committed counters belong to the default Llama-3-70B run.
+            "traffic": counter_traffic(os.path.dirname(os.path.abspath(__file__)), part_tokens)
             if (args.workload == "llama3_70b" and not args.kv_fp8 and not args.num_q_heads
-                and not args.fixed_len and not args.contiguous_blocks
-                and part_tokens == 2048) else None,
+                and not args.fixed_len and not args.contiguous_blocks) else None,
         },
         "copy_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
         "read_ceilings_GBps": rceiling,
