@@ -632,7 +632,9 @@ def bench_window(args, torch, pa, sess, w, B, stream):
         "data": "synthetic (seeded N(0,1) K/V/Q, seeded block permutation)",
         "config": {"workload": args.workload + "_window", "window": args.window,
                    "algorithmic_bytes_per_step": B,
-                   "partition_tokens": args.partition or pa.pa_decode_default_partition(sess.pool, w.num_q_heads)},
+                   # windowed calls take at most 2048-token partitions by default
+                   "partition_tokens": args.partition or min(
+                       pa.pa_decode_default_partition(sess.pool, w.num_q_heads), 2048)},
         "tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
         "kernel_ms": {"decode_window (plan + partitions + merge)": round(dec_ms, 5)},
         "roofline": {"bound": "hbm", "kernel": "pa_cache_and_decode_window (write + plan, partitions, merge)", "achieved": round(achieved, 2),

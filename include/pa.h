@@ -332,8 +332,11 @@ int64_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t
  * num_q_heads (host only, no GPU call): 4096 tokens for fp16 and bf16 caches at groups
  * (num_q_heads / num_kv_heads) of 8, 2048 for fp16 and bf16 at groups of 4 and for e4m3
  * caches at groups of 4 or 8; otherwise 1024 / element bytes tokens (512 for fp16/bf16,
- * 1024 for e4m3, 256 for fp32).  Returns PA_E_INVAL (negative) for a
- * NULL pool or num_q_heads that is not a positive multiple of num_kv_heads. */
+ * 1024 for e4m3, 256 for fp32).  Windowed calls (pa_decode_window,
+ * pa_cache_and_decode_window) take at most 2048 by default, and
+ * pa_decode_workspace_bytes with partition_tokens = 0 sizes for the smaller of the two, so
+ * that one workspace serves both.  Returns PA_E_INVAL (negative) for a NULL pool or
+ * num_q_heads that is not a positive multiple of num_kv_heads. */
 int32_t pa_decode_default_partition(const pa_pool* pool, int32_t num_q_heads);
 int pa_decode_plan(pa_pool* pool, int32_t layer, const void* q, int32_t num_seqs,
                    int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks,
